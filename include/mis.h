@@ -1,0 +1,196 @@
+/*
+ * mis.h - C ABI of the multiple-item scoring (MIS) hot path for AMD Instinct
+ * MI355X (gfx950 / CDNA4).
+ *
+ * The method (From Generation to Scoring: Scaling LLM-Based Semantic Labeling
+ * at LinkedIn, §4.1, Eq. 3 and Eq. 4): one prefill packs a shared query
+ * prefix q and N candidate items c_1..c_N, each closed by a delimiter token
+ * (LinkedIn SGLang blog, "Multi-item-scoring" section). Under the MIS mask
+ * every prefix token attends causally to the prefix, and every item token
+ * attends to the whole prefix plus the earlier tokens of its own item, never
+ * to another item. Position ids restart at Lq in every item. The label
+ * log-probabilities of an item are read from the next-token logits at its
+ * last token (its closing delimiter): one row of K label scores per item, in
+ * input order, columns in the requested label order (Scaling JEV-like
+ * Decision Models with SGLang, "Getting Started with the Score API").
+ *
+ * Three stream-ordered calls:
+ *   mis_build_segments    host metadata -> per-token item/position ids,
+ *                         per-item readout positions, per-tile classes
+ *   mis_attention_prefill MIS prefill attention (skips fully masked tiles)
+ *   mis_score_labels      readout gather -> LM head -> full-vocab logsumexp
+ *                         -> label log-probs
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Return value: MIS_OK (0) or a negative MIS_ERR_* code. On error the
+ *   thread-local text of mis_last_error() says what was wrong. All argument
+ *   and metadata checks run on the host before anything is enqueued, so a
+ *   call that fails its checks has no effect on the device.
+ * - "stream" is a hipStream_t passed as void* (NULL = the default stream).
+ *   Every device write is enqueued on that stream; results are ready once the
+ *   stream has been synchronised.
+ * - The library never allocates device memory. The caller owns every device
+ *   buffer; the *_bytes queries give the sizes.
+ * - Packed ("varlen") token-major layout: request r owns packed tokens
+ *   [cu_seqlens[r], cu_seqlens[r+1]); its first prefix_lens[r] tokens are the
+ *   prefix, then its items follow back to back in input order. Items are
+ *   numbered globally, request by request (row order of the scores).
+ * - Integer sizes are int32; every total must fit in int32.
+ */
+#ifndef MIS_H_
+#define MIS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MIS_OK 0
+#define MIS_ERR_ARG (-1)         /* null pointer, negative size, Hq % Hkv != 0, ... */
+#define MIS_ERR_SEGMENTS (-2)    /* malformed request/item metadata */
+#define MIS_ERR_LABEL (-3)       /* K < 1, K > MIS_MAX_LABELS, label id outside [0, V) */
+#define MIS_ERR_WORKSPACE (-4)   /* a caller buffer is smaller than its size query */
+#define MIS_ERR_UNSUPPORTED (-5) /* shape / dtype / tile combination not compiled */
+#define MIS_ERR_HIP (-6)         /* the HIP runtime reported an error (incl. no device) */
+
+#define MIS_MAX_LABELS 256
+
+/* Element type of Q/K/V/O, hidden states and LM head. */
+typedef enum { MIS_F32 = 0, MIS_BF16 = 1 } mis_dtype;
+
+/*
+ * Segment descriptors, filled by mis_build_segments. Host struct; the
+ * pointers are device addresses inside the caller's dev_buf, which must stay
+ * alive (and unmodified) for as long as the struct is used.
+ */
+typedef struct mis_segments {
+  int32_t num_requests; /* B */
+  int32_t total_tokens; /* T = cu_seqlens[B] */
+  int32_t total_items;  /* N */
+  int32_t block_m;      /* query-tile height of the tile classes */
+  int32_t block_n;      /* key-tile width of the tile classes */
+  int32_t num_tiles;    /* sum over requests of ceil(T_r/bm) * ceil(T_r/bn) */
+  int32_t num_work;     /* sum over requests of ceil(T_r/bm): query tiles */
+  int32_t max_seqlen;   /* max_r T_r */
+  /* per request */
+  const int32_t *cu_seqlens;  /* [B+1] packed token offsets */
+  const int32_t *prefix_lens; /* [B]   Lq of each request */
+  const int32_t *cu_items;    /* [B+1] global item offsets */
+  const int32_t *cu_tiles;    /* [B+1] tile offsets into tile_class */
+  /* per item */
+  const int32_t *item_begin;  /* [N] packed index of the item's first token */
+  const int32_t *readout_pos; /* [N] packed index of the item's last token (closing delimiter) */
+  /* per token */
+  const int32_t *item_id;     /* [T] -1 for prefix tokens, else global item index */
+  const int32_t *pos_id;      /* [T] prefix token u -> u; item offset d -> Lq + d */
+  /* per tile, request-major then query-tile-major:
+     0 = no visible cell, 1 = partly visible, 2 = every in-range cell visible */
+  const int8_t *tile_class;   /* [num_tiles] */
+  /* per query tile, longest first: {request, query tile, end of the prefix
+     key-tile range, first key tile of the own-item range} */
+  const int32_t *work;        /* [num_work * 4] */
+} mis_segments;
+
+/*
+ * Device bytes mis_build_segments needs for this metadata and tile shape.
+ * cu_seqlens_h: host [B+1]. Errors: ARG, SEGMENTS (offsets), UNSUPPORTED
+ * (block_m / block_n not positive multiples of 16, or above 256).
+ */
+int mis_segments_bytes(int32_t num_requests, const int32_t *cu_seqlens_h, int32_t total_items,
+                       int32_t block_m, int32_t block_n, size_t *bytes);
+
+/*
+ * Build the segment descriptors of a packed MIS batch (paper §4.1: Eq. 3
+ * packing, the reused position-id rule and the Eq. 4 mask; SGLang blog's
+ * delimiter-closed items). Per-token ids, readout positions and tile classes
+ * are computed by GPU kernels; the host validates the metadata, orders the
+ * query tiles longest first and stages everything with one copy.
+ *
+ * In (host, read before return; the caller may free them afterwards):
+ *   cu_seqlens_h[B+1]  non-decreasing, cu_seqlens_h[0] = 0, every T_r >= 1
+ *   prefix_lens_h[B]   0 <= Lq_r <= T_r
+ *   cu_items_h[B+1]    non-decreasing, cu_items_h[0] = 0, cu_items_h[B] = N
+ *   item_starts_h[N]   request-relative item starts: the first item of r
+ *                      starts at Lq_r, starts strictly increase inside r, and
+ *                      each item ends at the next start (the last at T_r);
+ *                      a request with no items must have Lq_r = T_r
+ *   block_m, block_n   tile shape of the tile classes; mis_attention_prefill
+ *                      requires the shape mis_attention_tile_shape returns
+ * Out:
+ *   dev_buf/dev_bytes  caller's device buffer, >= mis_segments_bytes
+ *   out                host struct, filled on success
+ * Errors: ARG, SEGMENTS, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int mis_build_segments(int32_t num_requests, const int32_t *cu_seqlens_h,
+                       const int32_t *prefix_lens_h, const int32_t *cu_items_h,
+                       const int32_t *item_starts_h, int32_t block_m, int32_t block_n,
+                       void *dev_buf, size_t dev_bytes, mis_segments *out, void *stream);
+
+/*
+ * Tile shape (block_m x block_n) that mis_attention_prefill uses for this
+ * dtype and head configuration; build the segments with it.
+ * Errors: ARG, UNSUPPORTED.
+ */
+int mis_attention_tile_shape(mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                             int32_t *block_m, int32_t *block_n);
+
+/*
+ * MIS prefill attention: O = softmax(scale * Q K^T + M) V per query head,
+ * M the Eq. 4 mask of paper §4.1 inside each request, no attention across
+ * requests. Query head h reads KV head floor(h * hkv / hq) (contiguous GQA
+ * groups). Key tiles with no visible cell are never loaded; per-cell masking
+ * runs only in partly visible tiles.
+ *
+ * q [T, hq, D], k and v [T, hkv, D], o [T, hq, D]: device, token-major,
+ * contiguous, element type dt (bf16 uses fp32 accumulation and fp32 softmax;
+ * P and O are rounded to bf16 to nearest even). softmax_scale <= 0 selects
+ * 1/sqrt(D). D must be 64 or 128; hq % hkv == 0.
+ * Errors: ARG, UNSUPPORTED (D, dt, or seg tile shape), HIP.
+ */
+int mis_attention_prefill(const mis_segments *seg, const void *q, const void *k, const void *v,
+                          void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                          float softmax_scale, void *stream);
+
+/*
+ * Device workspace bytes of mis_score_labels for N items, vocabulary V,
+ * K labels, hidden size H and element type dt. Errors: ARG, LABEL.
+ */
+int mis_score_workspace_bytes(int32_t num_items, int32_t vocab, int32_t num_labels,
+                              int32_t hidden, mis_dtype dt, size_t *bytes);
+
+/*
+ * Label scores of every item (paper §3.3, Eq. 2; JEV post, Score API with
+ * label_token_ids and apply_softmax; full-vocabulary normalisation is kept).
+ * For item n, h_n = hidden[seg->readout_pos[n]] and z_n = lm_head h_n over
+ * the whole vocabulary. Without apply_softmax, scores[n,k] = z_n[label_k] -
+ * logsumexp(z_n) (a log-probability <= 0); with apply_softmax, scores[n,:]
+ * is the softmax of z_n over the K label ids.
+ *
+ * hidden [T, H] and lm_head [V, H]: device, row-major, element type dt; only
+ * readout rows of hidden are read. label_ids_h: host [K], each in [0, V);
+ * duplicates allowed. scores: device float32 [N, K], row n = item n (global
+ * input order), column k = label_ids_h[k]; may be NULL when N = 0 (the call
+ * then only validates its arguments). ws/ws_bytes: device workspace of
+ * at least mis_score_workspace_bytes.
+ * Errors: ARG, LABEL, WORKSPACE, UNSUPPORTED, HIP.
+ */
+int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden_size,
+                     const void *lm_head, int32_t vocab, mis_dtype dt, const int32_t *label_ids_h,
+                     int32_t num_labels, int32_t apply_softmax, float *scores, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* Text of the last error on this thread ("" if none). Never NULL. */
+const char *mis_last_error(void);
+
+/* Library version string. */
+const char *mis_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIS_H_ */

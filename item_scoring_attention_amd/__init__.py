@@ -1,0 +1,38 @@
+"""Multiple-item scoring (MIS) hot path for AMD Instinct MI355X (gfx950).
+
+The computation lives in ``libmis.so`` (HIP kernels behind the C ABI of
+``include/mis.h``); this package is its ctypes binding. The three calls:
+
+* ``mis_build_segments``: per-token item/position ids, readout positions and
+  per-tile classes from prefix lengths and item offsets;
+* ``mis_attention_prefill``: MIS prefill attention on bf16 MFMA (or fp32);
+* ``mis_score_labels``: readout gather, LM-head contraction and full-vocab
+  logsumexp, writing one label-score row per item.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    MIS_BF16,
+    MIS_ERR_ARG,
+    MIS_ERR_HIP,
+    MIS_ERR_LABEL,
+    MIS_ERR_SEGMENTS,
+    MIS_ERR_UNSUPPORTED,
+    MIS_ERR_WORKSPACE,
+    MIS_F32,
+    MIS_MAX_LABELS,
+    MIS_OK,
+    MisError,
+    MisSegments,
+    MisValueError,
+    SIGNATURES,
+    Segments,
+    last_error,
+    load,
+    mis_attention_prefill,
+    mis_attention_tile_shape,
+    mis_build_segments,
+    mis_score_labels,
+    mis_score_workspace_bytes,
+    mis_segments_bytes,
+    version,
+)

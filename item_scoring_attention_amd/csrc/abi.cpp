@@ -1,0 +1,343 @@
+// Host side of the C ABI: argument and metadata validation (before anything
+// is enqueued), device-buffer carving, query-tile scheduling, launch dispatch
+// and the thread-local error text.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mis_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return MIS_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(MIS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool valid_block(int32_t b) { return b >= 16 && b <= 256 && b % 16 == 0; }
+
+// Offsets of every array inside the caller's segment buffer. The first
+// region ("stage") is one host->device copy; the rest is written by kernels.
+struct SegLayout {
+  size_t cu_seqlens, prefix_lens, cu_items, cu_tiles, item_starts, work, stage_end;
+  size_t item_begin, readout_pos, item_id, pos_id, tile_class, total;
+};
+
+SegLayout seg_layout(int64_t B, int64_t T, int64_t N, int64_t tiles, int64_t work) {
+  SegLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.cu_seqlens = take(sizeof(int32_t) * (B + 1));
+  L.prefix_lens = take(sizeof(int32_t) * B);
+  L.cu_items = take(sizeof(int32_t) * (B + 1));
+  L.cu_tiles = take(sizeof(int32_t) * (B + 1));
+  L.item_starts = take(sizeof(int32_t) * std::max<int64_t>(N, 1));
+  L.work = take(sizeof(int32_t) * 4 * std::max<int64_t>(work, 1));
+  L.stage_end = off;
+  L.item_begin = take(sizeof(int32_t) * std::max<int64_t>(N, 1));
+  L.readout_pos = take(sizeof(int32_t) * std::max<int64_t>(N, 1));
+  L.item_id = take(sizeof(int32_t) * T);
+  L.pos_id = take(sizeof(int32_t) * T);
+  L.tile_class = take(sizeof(int8_t) * std::max<int64_t>(tiles, 1));
+  L.total = off;
+  return L;
+}
+
+// Checks cu_seqlens and returns tile and query-tile counts.
+int check_seqlens(int32_t B, const int32_t *cu, int32_t bm, int32_t bn, int64_t *tiles,
+                  int64_t *work, int32_t *max_len) {
+  if (B < 1) return fail(MIS_ERR_ARG, "num_requests must be >= 1 (got %d)", B);
+  if (!cu) return fail(MIS_ERR_ARG, "cu_seqlens is NULL");
+  if (!valid_block(bm) || !valid_block(bn))
+    return fail(MIS_ERR_UNSUPPORTED, "block_m/block_n must be multiples of 16 in [16, 256] (got %d x %d)",
+                bm, bn);
+  if (cu[0] != 0) return fail(MIS_ERR_SEGMENTS, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+  int64_t t = 0, w = 0;
+  int32_t mx = 0;
+  for (int32_t r = 0; r < B; ++r) {
+    int64_t len = int64_t(cu[r + 1]) - int64_t(cu[r]);
+    if (len < 1)
+      return fail(MIS_ERR_SEGMENTS, "request %d has %lld tokens; cu_seqlens must strictly increase",
+                  r, (long long)len);
+    t += ceil_div(len, bm) * ceil_div(len, bn);
+    w += ceil_div(len, bm);
+    mx = std::max<int32_t>(mx, int32_t(len));
+  }
+  if (t > INT32_MAX) return fail(MIS_ERR_SEGMENTS, "tile count %lld overflows int32", (long long)t);
+  *tiles = t;
+  *work = w;
+  *max_len = mx;
+  return MIS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mis_last_error(void) { return g_error.c_str(); }
+
+const char *mis_version(void) { return "mis-gfx950 0.1"; }
+
+int mis_segments_bytes(int32_t num_requests, const int32_t *cu_seqlens_h, int32_t total_items,
+                       int32_t block_m, int32_t block_n, size_t *bytes) {
+  if (!bytes) return fail(MIS_ERR_ARG, "bytes is NULL");
+  if (total_items < 0) return fail(MIS_ERR_ARG, "total_items must be >= 0");
+  int64_t tiles, work;
+  int32_t mx;
+  int rc = check_seqlens(num_requests, cu_seqlens_h, block_m, block_n, &tiles, &work, &mx);
+  if (rc) return rc;
+  *bytes = seg_layout(num_requests, cu_seqlens_h[num_requests], total_items, tiles, work).total;
+  return ok();
+}
+
+int mis_build_segments(int32_t B, const int32_t *cu_seqlens_h, const int32_t *prefix_lens_h,
+                       const int32_t *cu_items_h, const int32_t *item_starts_h, int32_t block_m,
+                       int32_t block_n, void *dev_buf, size_t dev_bytes, mis_segments *out,
+                       void *stream) {
+  if (!out) return fail(MIS_ERR_ARG, "out is NULL");
+  if (!prefix_lens_h || !cu_items_h) return fail(MIS_ERR_ARG, "prefix_lens or cu_items is NULL");
+  if (!dev_buf) return fail(MIS_ERR_ARG, "dev_buf is NULL");
+  int64_t tiles, work;
+  int32_t max_len;
+  int rc = check_seqlens(B, cu_seqlens_h, block_m, block_n, &tiles, &work, &max_len);
+  if (rc) return rc;
+  const int32_t T = cu_seqlens_h[B];
+  if (cu_items_h[0] != 0) return fail(MIS_ERR_SEGMENTS, "cu_items[0] must be 0 (got %d)", cu_items_h[0]);
+  for (int32_t r = 0; r < B; ++r)
+    if (cu_items_h[r + 1] < cu_items_h[r])
+      return fail(MIS_ERR_SEGMENTS, "cu_items must be non-decreasing (request %d)", r);
+  const int32_t N = cu_items_h[B];
+  if (N > 0 && !item_starts_h) return fail(MIS_ERR_ARG, "item_starts is NULL");
+
+  // Metadata checks: items tile [Lq, T_r) contiguously, in order.
+  for (int32_t r = 0; r < B; ++r) {
+    const int32_t Tr = cu_seqlens_h[r + 1] - cu_seqlens_h[r];
+    const int32_t lq = prefix_lens_h[r];
+    if (lq < 0 || lq > Tr)
+      return fail(MIS_ERR_SEGMENTS, "request %d: prefix length %d outside [0, %d]", r, lq, Tr);
+    const int32_t a = cu_items_h[r], b = cu_items_h[r + 1];
+    if (a == b) {
+      if (lq != Tr)
+        return fail(MIS_ERR_SEGMENTS, "request %d has no items but prefix %d != length %d", r, lq, Tr);
+      continue;
+    }
+    if (item_starts_h[a] != lq)
+      return fail(MIS_ERR_SEGMENTS, "request %d: first item starts at %d, not at the prefix length %d",
+                  r, item_starts_h[a], lq);
+    for (int32_t i = a; i < b; ++i) {
+      const int32_t end = (i + 1 < b) ? item_starts_h[i + 1] : Tr;
+      if (end <= item_starts_h[i] || end > Tr)
+        return fail(MIS_ERR_SEGMENTS,
+                    "request %d: item %d [%d, %d) is empty, out of order or outside the request",
+                    r, i, item_starts_h[i], end);
+    }
+  }
+
+  const SegLayout L = seg_layout(B, T, N, tiles, work);
+  if (dev_bytes < L.total)
+    return fail(MIS_ERR_WORKSPACE, "dev_bytes %zu < required %zu", dev_bytes, L.total);
+
+  // Host image of the staged region.
+  std::vector<uint8_t> img(L.stage_end, 0);
+  auto put = [&](size_t off, const int32_t *src, size_t n) {
+    if (n) std::memcpy(img.data() + off, src, n * sizeof(int32_t));
+  };
+  put(L.cu_seqlens, cu_seqlens_h, B + 1);
+  put(L.prefix_lens, prefix_lens_h, B);
+  put(L.cu_items, cu_items_h, B + 1);
+  put(L.item_starts, item_starts_h, N);
+  int32_t *cu_tiles = reinterpret_cast<int32_t *>(img.data() + L.cu_tiles);
+  cu_tiles[0] = 0;
+
+  // Query-tile work list. For query tile [j0, j1) of request r the visible
+  // keys are the prefix keys [0, min(Lq, j1)) and, for item rows, the keys
+  // from the start of the item holding row max(j0, Lq) up to j1; key tiles
+  // strictly between the two ranges hold only other items' tokens and are
+  // never visited. Ordered by visited-tile count, longest first.
+  struct Work {
+    int32_t r, qt, a_end, b_lo, cost;
+  };
+  std::vector<Work> wl;
+  wl.reserve(size_t(work));
+  for (int32_t r = 0; r < B; ++r) {
+    const int32_t Tr = cu_seqlens_h[r + 1] - cu_seqlens_h[r];
+    const int32_t lq = prefix_lens_h[r];
+    const int32_t nqt = int32_t(ceil_div(Tr, block_m)), nkt = int32_t(ceil_div(Tr, block_n));
+    cu_tiles[r + 1] = cu_tiles[r] + nqt * nkt;
+    const int32_t a = cu_items_h[r], b = cu_items_h[r + 1];
+    for (int32_t qt = 0; qt < nqt; ++qt) {
+      const int32_t j0 = qt * block_m, j1 = std::min(Tr, j0 + block_m);
+      int32_t a_end = int32_t(ceil_div(std::min(lq, j1), block_n));
+      const int32_t b_hi = int32_t(ceil_div(j1, block_n));
+      int32_t b_lo = b_hi;
+      if (j1 > lq) {
+        const int32_t first_row = std::max(j0, lq);
+        // start of the item that holds first_row
+        const int32_t *s = item_starts_h + a;
+        const int32_t idx = int32_t(std::upper_bound(s, s + (b - a), first_row) - s) - 1;
+        b_lo = s[idx] / block_n;
+      }
+      if (b_lo <= a_end) {  // ranges touch: one contiguous range
+        a_end = std::max(a_end, b_hi);
+        b_lo = b_hi;
+      }
+      const int32_t cost = a_end + (b_hi - std::max(b_lo, a_end));
+      wl.push_back({r, qt, a_end, b_lo, cost});
+    }
+  }
+  std::stable_sort(wl.begin(), wl.end(), [](const Work &x, const Work &y) { return x.cost > y.cost; });
+  int32_t *wdst = reinterpret_cast<int32_t *>(img.data() + L.work);
+  for (size_t i = 0; i < wl.size(); ++i) {
+    wdst[4 * i + 0] = wl[i].r;
+    wdst[4 * i + 1] = wl[i].qt;
+    wdst[4 * i + 2] = wl[i].a_end;
+    wdst[4 * i + 3] = wl[i].b_lo;
+  }
+
+  uint8_t *base = static_cast<uint8_t *>(dev_buf);
+  mis_segments s{};
+  s.num_requests = B;
+  s.total_tokens = T;
+  s.total_items = N;
+  s.block_m = block_m;
+  s.block_n = block_n;
+  s.num_tiles = int32_t(tiles);
+  s.num_work = int32_t(work);
+  s.max_seqlen = max_len;
+  s.cu_seqlens = reinterpret_cast<const int32_t *>(base + L.cu_seqlens);
+  s.prefix_lens = reinterpret_cast<const int32_t *>(base + L.prefix_lens);
+  s.cu_items = reinterpret_cast<const int32_t *>(base + L.cu_items);
+  s.cu_tiles = reinterpret_cast<const int32_t *>(base + L.cu_tiles);
+  s.item_begin = reinterpret_cast<const int32_t *>(base + L.item_begin);
+  s.readout_pos = reinterpret_cast<const int32_t *>(base + L.readout_pos);
+  s.item_id = reinterpret_cast<const int32_t *>(base + L.item_id);
+  s.pos_id = reinterpret_cast<const int32_t *>(base + L.pos_id);
+  s.tile_class = reinterpret_cast<const int8_t *>(base + L.tile_class);
+  s.work = reinterpret_cast<const int32_t *>(base + L.work);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // Pageable source: the runtime stages it before returning, so the image
+  // may be released when this function returns.
+  hipError_t e = hipMemcpyAsync(dev_buf, img.data(), L.stage_end, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "staging segment metadata");
+  e = mis::launch_segments(s, reinterpret_cast<const int32_t *>(base + L.item_starts), st);
+  if (e != hipSuccess) return hip_fail(e, "segment builder launch");
+  *out = s;
+  return ok();
+}
+
+int mis_attention_tile_shape(mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                             int32_t *block_m, int32_t *block_n) {
+  if (!block_m || !block_n) return fail(MIS_ERR_ARG, "block_m or block_n is NULL");
+  if (hq < 1 || hkv < 1 || hq % hkv)
+    return fail(MIS_ERR_ARG, "need hq >= 1, hkv >= 1 and hq %% hkv == 0 (got %d, %d)", hq, hkv);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(MIS_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (dt != MIS_F32 && dt != MIS_BF16) return fail(MIS_ERR_UNSUPPORTED, "unknown dtype %d", int(dt));
+  if (dt == MIS_BF16 && head_dim != 128)
+    return fail(MIS_ERR_UNSUPPORTED, "bf16 attention is built for head_dim 128 (got %d)", head_dim);
+  *block_m = mis::kAttnBlockM;
+  *block_n = mis::kAttnBlockN;
+  return ok();
+}
+
+int mis_attention_prefill(const mis_segments *seg, const void *q, const void *k, const void *v,
+                          void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                          float softmax_scale, void *stream) {
+  if (!seg) return fail(MIS_ERR_ARG, "seg is NULL");
+  if (!q || !k || !v || !o) return fail(MIS_ERR_ARG, "q, k, v and o must be non-NULL");
+  int32_t bm, bn;
+  int rc = mis_attention_tile_shape(dt, hq, hkv, head_dim, &bm, &bn);
+  if (rc) return rc;
+  if (seg->block_m != bm || seg->block_n != bn)
+    return fail(MIS_ERR_UNSUPPORTED, "segments built for %d x %d tiles; this kernel needs %d x %d",
+                seg->block_m, seg->block_n, bm, bn);
+  if (seg->total_tokens < 1 || !seg->work || !seg->tile_class || !seg->item_id)
+    return fail(MIS_ERR_ARG, "seg is not a built segment descriptor");
+  if (!std::isfinite(softmax_scale)) return fail(MIS_ERR_ARG, "softmax_scale is not finite");
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = dt == MIS_BF16
+                     ? mis::launch_attention_bf16(*seg, q, k, v, o, hq, hkv, head_dim, scale, st)
+                     : mis::launch_attention_f32(*seg, static_cast<const float *>(q),
+                                                 static_cast<const float *>(k),
+                                                 static_cast<const float *>(v), static_cast<float *>(o),
+                                                 hq, hkv, head_dim, scale, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+int mis_score_workspace_bytes(int32_t num_items, int32_t vocab, int32_t num_labels, int32_t hidden,
+                              mis_dtype dt, size_t *bytes) {
+  if (!bytes) return fail(MIS_ERR_ARG, "bytes is NULL");
+  if (num_items < 0 || vocab < 1 || hidden < 1)
+    return fail(MIS_ERR_ARG, "need num_items >= 0, vocab >= 1, hidden >= 1");
+  if (num_labels < 1 || num_labels > MIS_MAX_LABELS)
+    return fail(MIS_ERR_LABEL, "num_labels must be in [1, %d] (got %d)", MIS_MAX_LABELS, num_labels);
+  if (dt != MIS_F32 && dt != MIS_BF16) return fail(MIS_ERR_UNSUPPORTED, "unknown dtype %d", int(dt));
+  const size_t nvt = size_t(mis::score_vocab_tiles(vocab));
+  const size_t n = size_t(std::max(num_items, 1));
+  *bytes = align_up(sizeof(float) * n * nvt) * 2 + align_up(sizeof(float) * n * num_labels);
+  return ok();
+}
+
+int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden_size,
+                     const void *lm_head, int32_t vocab, mis_dtype dt, const int32_t *label_ids_h,
+                     int32_t num_labels, int32_t apply_softmax, float *scores, void *ws,
+                     size_t ws_bytes, void *stream) {
+  if (!seg) return fail(MIS_ERR_ARG, "seg is NULL");
+  if (!hidden || !lm_head || !ws) return fail(MIS_ERR_ARG, "hidden, lm_head and ws must be non-NULL");
+  if (!scores && seg->total_items > 0) return fail(MIS_ERR_ARG, "scores is NULL");
+  if (!label_ids_h) return fail(MIS_ERR_ARG, "label_ids is NULL");
+  size_t need;
+  int rc = mis_score_workspace_bytes(seg->total_items, vocab, num_labels, hidden_size, dt, &need);
+  if (rc) return rc;
+  for (int32_t i = 0; i < num_labels; ++i)
+    if (label_ids_h[i] < 0 || label_ids_h[i] >= vocab)
+      return fail(MIS_ERR_LABEL, "label id %d at position %d outside [0, %d)", label_ids_h[i], i, vocab);
+  if (ws_bytes < need) return fail(MIS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, need);
+  if (dt == MIS_BF16 && hidden_size % 32)
+    return fail(MIS_ERR_UNSUPPORTED, "bf16 scoring needs hidden_size %% 32 == 0 (got %d)", hidden_size);
+  if (seg->total_items == 0) return ok();
+  if (!seg->readout_pos) return fail(MIS_ERR_ARG, "seg is not a built segment descriptor");
+  mis::LabelArgs la{};
+  la.k = num_labels;
+  std::memcpy(la.ids, label_ids_h, sizeof(int32_t) * num_labels);
+  hipError_t e = mis::launch_score(*seg, hidden, hidden_size, lm_head, vocab, dt, la,
+                                   apply_softmax ? 1 : 0, scores, static_cast<float *>(ws),
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "scoring launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal declarations shared by the host ABI (abi.cpp) and the HIP kernel
+// sources. Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "mis.h"
+
+namespace mis {
+
+// Tile shape of the bf16 MFMA attention kernel: 64 query tokens x 64 keys.
+constexpr int kAttnBlockM = 64;
+constexpr int kAttnBlockN = 64;
+
+// Vocabulary rows per workgroup of the scoring kernels (one partial
+// (max, sum-exp) pair per item and vocabulary tile).
+constexpr int kScoreBlockV = 128;
+
+struct LabelArgs {
+  int32_t k;
+  int32_t ids[MIS_MAX_LABELS];
+};
+
+// Builder: per-item begin/readout, per-token item/position ids, per-tile
+// classes. item_starts is request-relative (as the caller gave it).
+hipError_t launch_segments(const mis_segments &seg, const int32_t *item_starts_dev,
+                           hipStream_t stream);
+
+hipError_t launch_attention_f32(const mis_segments &seg, const float *q, const float *k,
+                                const float *v, float *o, int hq, int hkv, int d, float scale,
+                                hipStream_t stream);
+
+hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const void *k,
+                                 const void *v, void *o, int hq, int hkv, int d, float scale,
+                                 hipStream_t stream);
+
+// Scoring workspace layout: partial maxima [N][nvt], partial sum-exp
+// [N][nvt], label logits [N][K] (all float32).
+inline int score_vocab_tiles(int vocab) { return (vocab + kScoreBlockV - 1) / kScoreBlockV; }
+
+hipError_t launch_score(const mis_segments &seg, const void *hidden, int h, const void *lm_head,
+                        int vocab, mis_dtype dt, const LabelArgs &labels, int apply_softmax,
+                        float *scores, float *ws, hipStream_t stream);
+
+}  // namespace mis

@@ -1,0 +1,87 @@
+"""Helpers shared by the GPU parity tests: uploads, library calls, row sampling.
+
+Inputs come from ``workloads`` (seeded); expected values come from
+``oracle`` only. The library is called through its C ABI binding.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import item_scoring_attention_amd as mis
+import oracle
+import workloads
+
+# Tolerances: max abs error (fp32 workloads 1e-4; bf16 with fp32 accumulation
+# 2e-2 on attention outputs and 1e-2 on label log-probs).
+TOL_F32 = 1e-4
+TOL_BF16_ATTN = 2e-2
+TOL_BF16_SCORE = 1e-2
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(x: np.ndarray) -> torch.Tensor:
+    """numpy -> device tensor (uint16 arrays are bf16 bit patterns)."""
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """device tensor -> numpy (bf16 as uint16 bit patterns)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def segments_oracle(wl):
+    return oracle.build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts)
+
+
+def build(wl, dtype=None):
+    dt = mis.MIS_BF16 if (dtype or wl.dtype) == "bf16" else mis.MIS_F32
+    bm, bn = mis.mis_attention_tile_shape(dt, wl.hq, wl.hkv, wl.d)
+    seg = mis.mis_build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, bm, bn)
+    return seg
+
+
+def attention(wl, seg, q, k, v, scale=0.0):
+    o = mis.mis_attention_prefill(seg, dev(q), dev(k), dev(v), softmax_scale=scale)
+    torch.cuda.synchronize()
+    return o
+
+
+def sample_rows(wl, seg_o, per_request=24, seed=0):
+    """Packed query rows to check at full size: prefix ends, item edges, readouts, random."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    readout = seg_o["readout_pos"]
+    for r in range(wl.num_requests):
+        a, b = int(wl.cu_seqlens[r]), int(wl.cu_seqlens[r + 1])
+        lq = int(wl.prefix_lens[r])
+        cand = {a, b - 1, a + min(lq, b - a - 1), a + max(lq - 1, 0), a + min(63, b - a - 1),
+                a + min(64, b - a - 1)}
+        ia, ib = int(wl.cu_items[r]), int(wl.cu_items[r + 1])
+        if ib > ia:
+            for i in rng.choice(np.arange(ia, ib), size=min(4, ib - ia), replace=False):
+                cand.add(int(readout[i]))
+                cand.add(int(wl.item_starts[i]) + a)
+        extra = max(0, per_request - len(cand))
+        cand.update(int(x) for x in rng.integers(a, b, size=extra))
+        rows.extend(sorted(cand))
+    return np.asarray(sorted(set(rows)), dtype=np.int64)
+
+
+def hidden_with_sentinels(wl, readout_pos):
+    """[T, H] hidden states: N(0,1) rows at the readout positions, NaN elsewhere."""
+    vals = workloads.readout_values(wl)
+    if wl.dtype == "bf16":
+        hid = np.full((wl.total_tokens, wl.hidden), workloads.NAN_BF16, dtype=np.uint16)
+    else:
+        hid = np.full((wl.total_tokens, wl.hidden), np.nan, dtype=np.float32)
+    hid[np.asarray(readout_pos)] = vals
+    return hid

@@ -1,0 +1,187 @@
+"""C-ABI checks that need no GPU: symbols, size queries, host-side validation.
+
+Every malformed input below is rejected by the host checks before the
+library touches the HIP runtime, so nothing here reaches a device.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import item_scoring_attention_amd as mis
+from item_scoring_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mis.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mis_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = mis.load()
+    declared = _declared_functions()
+    assert set(declared) >= {"mis_build_segments", "mis_attention_prefill", "mis_score_labels"}
+    for name in declared:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+    assert mis.version().startswith("mis-gfx950")
+
+
+def test_struct_layout_matches_header():
+    # 8 int32 fields then 10 pointers
+    assert ctypes.sizeof(mis.MisSegments) == 8 * 4 + 10 * 8
+
+
+def _i32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _seg_bytes(cu, n, bm=64, bn=64):
+    lib = mis.load()
+    a, p = _i32(cu)
+    out = ctypes.c_size_t(0)
+    rc = lib.mis_segments_bytes(len(a) - 1, p, n, bm, bn, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_segments_bytes_grows_with_size_and_rejects_bad_input():
+    rc, small = _seg_bytes([0, 100], 4)
+    assert rc == 0 and small > 0
+    rc, big = _seg_bytes([0, 100, 5000], 80)
+    assert rc == 0 and big > small
+    assert _seg_bytes([0, 100], 4, bm=48, bn=24)[0] == mis.MIS_ERR_UNSUPPORTED
+    assert _seg_bytes([0, 100], 4, bm=512)[0] == mis.MIS_ERR_UNSUPPORTED
+    assert _seg_bytes([1, 100], 4)[0] == mis.MIS_ERR_SEGMENTS
+    assert _seg_bytes([0, 100, 100], 4)[0] == mis.MIS_ERR_SEGMENTS
+    assert _seg_bytes([0, 100], -1)[0] == mis.MIS_ERR_ARG
+
+
+def _build(cu, pl, ci, st, bm=64, bn=64, dev=0x1000, dev_bytes=1 << 30):
+    """Call mis_build_segments on the host; ``dev`` is never dereferenced for bad metadata."""
+    lib = mis.load()
+    a, pa = _i32(cu)
+    b, pb = _i32(pl)
+    c, pc = _i32(ci)
+    d, pd = _i32(st)
+    out = mis.MisSegments()
+    rc = lib.mis_build_segments(len(a) - 1, pa, pb, pc, pd if d.size else None, bm, bn,
+                                ctypes.c_void_p(dev), dev_bytes, ctypes.byref(out), None)
+    return rc, mis.last_error()
+
+
+@pytest.mark.parametrize(
+    "cu,pl,ci,st,code",
+    [
+        ([0, 20, 10], [4, 2], [0, 1, 2], [4, 2], mis.MIS_ERR_SEGMENTS),  # cu_seqlens decreasing
+        ([0, 20], [4], [0, 2], [5, 10], mis.MIS_ERR_SEGMENTS),  # first item != prefix length
+        ([0, 20], [4], [0, 2], [4, 25], mis.MIS_ERR_SEGMENTS),  # item beyond the request
+        ([0, 20], [4], [0, 3], [4, 10, 10], mis.MIS_ERR_SEGMENTS),  # empty item
+        ([0, 20], [4], [0, 3], [4, 12, 8], mis.MIS_ERR_SEGMENTS),  # out of order
+        ([0, 20], [21], [0, 0], [], mis.MIS_ERR_SEGMENTS),  # prefix longer than request
+        ([0, 20], [-1], [0, 1], [0], mis.MIS_ERR_SEGMENTS),  # negative prefix
+        ([0, 20], [10], [0, 0], [], mis.MIS_ERR_SEGMENTS),  # no items but prefix != length
+        ([0, 20], [4], [1, 2], [4], mis.MIS_ERR_SEGMENTS),  # cu_items[0] != 0
+        ([0, 20, 30], [4, 3], [0, 2, 1], [4, 9], mis.MIS_ERR_SEGMENTS),  # cu_items decreasing
+    ],
+)
+def test_build_rejects_malformed_metadata(cu, pl, ci, st, code):
+    rc, msg = _build(cu, pl, ci, st)
+    assert rc == code and msg
+
+
+def test_build_rejects_null_and_small_buffers():
+    rc, _ = _build([0, 20], [4], [0, 2], [4, 10], dev=0)
+    assert rc == mis.MIS_ERR_ARG
+    rc, msg = _build([0, 20], [4], [0, 2], [4, 10], dev_bytes=16)
+    assert rc == mis.MIS_ERR_WORKSPACE and "required" in msg
+    rc, _ = _build([0, 20], [4], [0, 2], [4, 10], bm=40)
+    assert rc == mis.MIS_ERR_UNSUPPORTED
+
+
+def test_tile_shape_query():
+    assert mis.mis_attention_tile_shape(mis.MIS_BF16, 32, 8, 128) == (64, 64)
+    assert mis.mis_attention_tile_shape(mis.MIS_F32, 4, 4, 64) == (64, 64)
+    with pytest.raises(ValueError):
+        mis.mis_attention_tile_shape(mis.MIS_BF16, 6, 4, 128)
+    with pytest.raises(RuntimeError):
+        mis.mis_attention_tile_shape(mis.MIS_BF16, 8, 8, 96)
+    with pytest.raises(RuntimeError):
+        mis.mis_attention_tile_shape(mis.MIS_BF16, 8, 8, 64)
+
+
+def _fake_seg(n_items=4, tokens=100, bm=64, bn=64):
+    s = mis.MisSegments()
+    s.num_requests, s.total_tokens, s.total_items = 1, tokens, n_items
+    s.block_m, s.block_n, s.num_tiles, s.num_work = bm, bn, 4, 2
+    s.work = s.tile_class = s.item_id = s.readout_pos = 0x1000
+    return s
+
+
+def test_attention_argument_errors():
+    lib = mis.load()
+    s = _fake_seg()
+    p = ctypes.c_void_p(0x1000)
+    call = lambda seg, q, dt, hq, hkv, d, sc=0.0: lib.mis_attention_prefill(
+        seg, q, p, p, p, dt, hq, hkv, d, sc, None)
+    assert call(None, p, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_ARG
+    assert call(ctypes.byref(s), None, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_ARG
+    assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 3, 128) == mis.MIS_ERR_ARG
+    assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 4, 80) == mis.MIS_ERR_UNSUPPORTED
+    assert call(ctypes.byref(s), p, 7, 8, 4, 128) == mis.MIS_ERR_UNSUPPORTED
+    assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 4, 128, float("nan")) == mis.MIS_ERR_ARG
+    s2 = _fake_seg(bm=32)
+    assert call(ctypes.byref(s2), p, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_UNSUPPORTED
+
+
+def test_score_argument_errors():
+    lib = mis.load()
+    s = _fake_seg()
+    p = ctypes.c_void_p(0x1000)
+    need = mis.mis_score_workspace_bytes(4, 1000, 2, 256, mis.MIS_BF16)
+    assert need > 0
+
+    def call(labels, K, ws_bytes=need, H=256, V=1000, dt=mis.MIS_BF16):
+        a, pa = _i32(labels)
+        return lib.mis_score_labels(ctypes.byref(s), p, H, p, V, dt, pa if a.size else None, K, 0,
+                                    p, p, ws_bytes, None)
+
+    assert call([3, 7], 0) == mis.MIS_ERR_LABEL
+    assert call([3, 7], 300) == mis.MIS_ERR_LABEL
+    assert call([3, 1000], 2) == mis.MIS_ERR_LABEL
+    assert call([-1, 5], 2) == mis.MIS_ERR_LABEL
+    assert call([3, 7], 2, ws_bytes=need - 1) == mis.MIS_ERR_WORKSPACE
+    assert call([3, 7], 2, H=100) == mis.MIS_ERR_UNSUPPORTED
+    assert call([], 2) == mis.MIS_ERR_ARG
+    assert lib.mis_score_labels(None, p, 256, p, 1000, mis.MIS_BF16, None, 2, 0, p, p, need,
+                                None) == mis.MIS_ERR_ARG
+
+
+def test_errors_raise_python_exceptions():
+    with pytest.raises(ValueError):
+        mis.mis_segments_bytes([0, 10, 5], 0, 64, 64)
+    with pytest.raises(RuntimeError):
+        mis.mis_segments_bytes([0, 10], 0, 64, 60)
+    with pytest.raises(ValueError):
+        mis.mis_score_workspace_bytes(4, 1000, 0, 64, mis.MIS_F32)
+
+
+def _gpu_visible():
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="checks the no-device path; a device is visible")
+def test_valid_call_without_a_device_reports_hip_error():
+    rc, msg = _build([0, 20], [4], [0, 2], [4, 10])
+    assert rc == mis.MIS_ERR_HIP and msg

@@ -1,0 +1,148 @@
+"""GPU MIS attention vs the fp64 oracle (element by element), plus SIS, order and determinism checks.
+
+Small shapes are compared on every output element; the full-size workloads
+on sampled query rows (every head, every dim) that the oracle computes one
+by one, in the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_common import (TOL_BF16_ATTN, TOL_F32, attention, build, host, sample_rows, say,
+                        segments_oracle)
+
+pytestmark = pytest.mark.gpu
+
+
+def _err(got, ref):
+    return float(np.abs(oracle.as_f64(got) - ref).max())
+
+
+def _run(wl, scale_q=1.0):
+    q, k, v = workloads.qkv(wl, scale_q=scale_q)
+    seg = build(wl)
+    o = host(attention(wl, seg, q, k, v))
+    return q, k, v, o
+
+
+def _full_check(wl, scale_q=1.0, tol=None):
+    tol = tol or (TOL_F32 if wl.dtype == "f32" else TOL_BF16_ATTN)
+    say(f"[attention full] {wl.name} T={wl.total_tokens} hq={wl.hq} hkv={wl.hkv}")
+    q, k, v, o = _run(wl, scale_q)
+    ref = oracle.attention(q, k, v, wl.cu_seqlens, segments_oracle(wl)["item_id"])
+    e = _err(o, ref)
+    say(f"  max abs err {e:.3e}")
+    assert np.isfinite(oracle.as_f64(o)).all()
+    assert e <= tol
+    return q, k, v, o
+
+
+def test_f32_tiny_config():
+    _full_check(workloads.config(1))
+
+
+def test_f32_d128_and_gqa():
+    wl = workloads.from_lengths("f32gqa", [37, 0], [[5, 1, 12], [3, 3]], dtype="f32", hq=6, hkv=2,
+                                d=128, seed=7)
+    _full_check(wl)
+
+
+@pytest.mark.parametrize("shape", [
+    ([130], [[9, 1, 33, 64, 2]], 8, 4),
+    ([0, 77, 200], [[40, 1, 1], [5, 70], [3] * 20], 8, 2),
+    ([65], [[]], 4, 2),  # T = 65: last query/key tile holds one token
+    ([129, 1], [[1, 1, 1], []], 16, 8),
+    ([300], [[17] * 12], 4, 4),  # G = 1 (MHA) uses the one-head workgroup
+    ([64, 63], [[64], [1, 1]], 6, 2),  # odd group size (3)
+])
+def test_bf16_small_shapes_all_elements(shape):
+    p, it, hq, hkv = shape
+    wl = workloads.from_lengths("small", p, it, hq=hq, hkv=hkv, d=128, seed=len(p) * 31 + hq)
+    _full_check(wl)
+
+
+def test_bf16_peaky_softmax():
+    # Q x 4 sharpens the softmax: exercises online-max raising and rescaling
+    wl = workloads.from_lengths("peaky", [700], [[20] * 30], hq=8, hkv=4, d=128, seed=9)
+    _full_check(wl, scale_q=4.0)
+
+
+def test_bf16_single_request_config_full():
+    _full_check(workloads.config(2))
+
+
+def _sampled_check(k_cfg, per_request):
+    wl = workloads.config(k_cfg)
+    say(f"[attention sampled] {wl.name} T={wl.total_tokens}")
+    q, k, v, o = _run(wl)
+    so = segments_oracle(wl)
+    rows = sample_rows(wl, so, per_request=per_request)
+    ref = oracle.attention(q, k, v, wl.cu_seqlens, so["item_id"], rows=rows)
+    e = _err(o[rows], ref)
+    say(f"  {len(rows)} rows, max abs err {e:.3e}")
+    assert np.isfinite(oracle.as_f64(o)).all()
+    assert e <= TOL_BF16_ATTN
+
+
+def test_bf16_profile_labeling_config_sampled():
+    _sampled_check(3, 96)
+
+
+def test_bf16_ragged_serving_config_sampled():
+    _sampled_check(4, 12)
+
+
+def test_bf16_long_prefix_config_sampled():
+    _sampled_check(5, 24)
+
+
+def test_mis_rows_equal_single_item_scoring():
+    # every item of a small batch, against [q; c_i] run alone under a causal mask
+    wl = workloads.from_lengths("sis", [96, 40], [[7, 30, 1, 12], [25, 2]], hq=8, hkv=4, d=128,
+                                seed=12)
+    q, k, v, o = _run(wl)
+    sis = oracle.sis_attention(q, k, v, wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts)
+    assert _err(o, sis) <= TOL_BF16_ATTN
+
+
+def test_f32_tiny_config_equals_single_item_scoring():
+    wl = workloads.config(1)
+    q, k, v, o = _run(wl)
+    sis = oracle.sis_attention(q, k, v, wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts)
+    assert _err(o, sis) <= TOL_F32
+
+
+def test_item_order_invariance():
+    lens = [9, 33, 1, 17, 64, 5]
+    perm = [3, 0, 5, 1, 4, 2]
+    wl = workloads.from_lengths("order", [150], [lens], hq=8, hkv=4, d=128, seed=13)
+    q, k, v, o = _run(wl)
+    wl2 = workloads.from_lengths("order2", [150], [[lens[p] for p in perm]], hq=8, hkv=4, d=128)
+    idx = list(range(150))
+    for p in perm:
+        s0 = int(wl.item_starts[p])
+        idx += list(range(s0, s0 + lens[p]))
+    idx = np.asarray(idx)
+    seg2 = build(wl2)
+    o2 = host(attention(wl2, seg2, q[idx], k[idx], v[idx]))
+    assert _err(o2, oracle.as_f64(o[idx])) <= TOL_BF16_ATTN
+
+
+def test_repeat_runs_are_bit_identical():
+    wl = workloads.config(2)
+    q, k, v = workloads.qkv(wl)
+    seg = build(wl)
+    a = host(attention(wl, seg, q, k, v))
+    b = host(attention(wl, seg, q, k, v))
+    assert np.array_equal(a, b)
+
+
+def test_explicit_softmax_scale():
+    wl = workloads.from_lengths("scale", [80], [[10, 20]], hq=8, hkv=4, d=128, seed=14)
+    q, k, v = workloads.qkv(wl)
+    seg = build(wl)
+    o = host(attention(wl, seg, q, k, v, scale=0.05))
+    ref = oracle.attention(q, k, v, wl.cu_seqlens, segments_oracle(wl)["item_id"], scale=0.05)
+    assert _err(o, ref) <= TOL_BF16_ATTN

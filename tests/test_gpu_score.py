@@ -1,0 +1,138 @@
+"""GPU label scoring vs the fp64 oracle: full-vocab log-probs, label softmax, edge cases.
+
+Hidden rows other than the items' readout rows hold NaN, so any read of a
+wrong row shows up as a NaN score.
+"""
+import numpy as np
+import pytest
+import torch
+
+import item_scoring_attention_amd as mis
+import oracle
+import workloads
+from gpu_common import (TOL_BF16_SCORE, TOL_F32, build, dev, hidden_with_sentinels, host, say,
+                        segments_oracle)
+
+pytestmark = pytest.mark.gpu
+
+
+def _score(wl, seg, hid, W, labels, apply_softmax=False):
+    s = mis.mis_score_labels(seg, dev(hid), dev(W), labels, apply_softmax=apply_softmax)
+    torch.cuda.synchronize()
+    return host(s).astype(np.float64)
+
+
+def _check_config(wl, items=None):
+    tol = TOL_F32 if wl.dtype == "f32" else TOL_BF16_SCORE
+    say(f"[score] {wl.name} N={wl.total_items} H={wl.hidden} V={wl.vocab} K={wl.num_labels}")
+    so = segments_oracle(wl)
+    seg = build(wl)
+    hid = hidden_with_sentinels(wl, so["readout_pos"])
+    W = workloads.lm_head(wl)
+    labels = workloads.label_ids(wl)
+    got = _score(wl, seg, hid, W, labels)
+    assert np.isfinite(got).all()
+    sel = np.arange(wl.total_items) if items is None else np.asarray(items)
+    ref = oracle.label_scores(hid, so["readout_pos"][sel], W, labels)
+    e = float(np.abs(got[sel] - ref).max())
+    say(f"  logp max abs err {e:.3e} over {len(sel)} items")
+    assert e <= tol
+    # log-probs are <= 0 and the label mass is at most one
+    assert (got <= tol).all()
+    assert (np.log(np.exp(got).sum(axis=1)) <= tol).all()
+    p = _score(wl, seg, hid, W, labels, apply_softmax=True)
+    refp = oracle.label_scores(hid, so["readout_pos"][sel], W, labels, apply_softmax=True)
+    ep = float(np.abs(p[sel] - refp).max())
+    say(f"  softmax max abs err {ep:.3e}")
+    assert ep <= tol
+    assert np.abs(p.sum(axis=1) - 1.0).max() <= 1e-5
+
+
+def test_tiny_f32_config():
+    _check_config(workloads.config(1))
+
+
+def test_single_request_config():
+    _check_config(workloads.config(2))
+
+
+def test_profile_labeling_config():
+    _check_config(workloads.config(3))
+
+
+def test_long_prefix_config_sampled_items():
+    wl = workloads.config(5)
+    rng = np.random.default_rng(5)
+    items = np.unique(np.concatenate([[0, wl.total_items - 1],
+                                      rng.choice(wl.total_items, 22, replace=False)]))
+    _check_config(wl, items=items)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_items,vocab", [(1, 1000), (37, 129), (65, 1000), (200, 300), (300, 1)])
+def test_item_and_vocab_edges(dtype, n_items, vocab):
+    # ragged vocabulary tiles, item tiles with a tail, labels at both vocabulary ends
+    lens = [3] * n_items
+    wl = workloads.from_lengths("edge", [10], [lens], dtype=dtype, hq=4, hkv=2, d=128, hidden=64,
+                                vocab=vocab, num_labels=1)
+    so = segments_oracle(wl)
+    seg = build(wl)
+    hid = hidden_with_sentinels(wl, so["readout_pos"])
+    W = workloads.lm_head(wl)
+    labels = sorted({0, vocab - 1, vocab // 2, 0})
+    got = _score(wl, seg, hid, W, labels)
+    ref = oracle.label_scores(hid, so["readout_pos"], W, labels)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16_SCORE
+    assert np.abs(got - ref).max() <= tol
+    if vocab == 1:
+        assert np.abs(got).max() <= tol  # a one-word vocabulary has log-prob 0
+
+
+def test_duplicate_labels_repeat_columns():
+    wl = workloads.from_lengths("dup", [20], [[4] * 5], hq=4, hkv=2, d=128, hidden=128, vocab=5000,
+                                num_labels=2)
+    so = segments_oracle(wl)
+    seg = build(wl)
+    hid = hidden_with_sentinels(wl, so["readout_pos"])
+    W = workloads.lm_head(wl)
+    labels = [17, 4999, 17]
+    got = _score(wl, seg, hid, W, labels)
+    assert np.array_equal(got[:, 0], got[:, 2])
+    ref = oracle.label_scores(hid, so["readout_pos"], W, labels)
+    assert np.abs(got - ref).max() <= TOL_BF16_SCORE
+
+
+def test_whole_vocab_as_labels_sums_to_one():
+    wl = workloads.from_lengths("all", [8], [[2] * 3], hq=4, hkv=2, d=128, hidden=64, vocab=256,
+                                num_labels=1)
+    so = segments_oracle(wl)
+    seg = build(wl)
+    hid = hidden_with_sentinels(wl, so["readout_pos"])
+    W = workloads.lm_head(wl)
+    got = _score(wl, seg, hid, W, list(range(256)))
+    assert np.abs(np.exp(got).sum(axis=1) - 1.0).max() <= 1e-4
+
+
+def test_chained_tiny_config_equals_single_item_scores():
+    # hidden := MIS attention output [T, Hq*D] (Hq*D == H == 256), read at each item's last token
+    wl = workloads.config(1)
+    q, k, v = workloads.qkv(wl)
+    seg = build(wl)
+    o = mis.mis_attention_prefill(seg, dev(q), dev(k), dev(v))
+    hid = o.reshape(wl.total_tokens, wl.hq * wl.d).contiguous()
+    W = workloads.lm_head(wl)
+    labels = workloads.label_ids(wl)
+    got = host(mis.mis_score_labels(seg, hid, dev(W), labels)).astype(np.float64)
+    sis = oracle.sis_scores(q, k, v, int(wl.prefix_lens[0]), wl.item_lengths().tolist(), W, labels)
+    assert np.abs(got - sis).max() <= TOL_F32
+
+
+def test_no_items_is_a_no_op():
+    wl = workloads.from_lengths("none", [50], [[]], hq=4, hkv=2, d=128, hidden=64, vocab=100,
+                                num_labels=1)
+    seg = build(wl)
+    hid = np.zeros((50, 64), dtype=np.uint16)
+    W = workloads.lm_head(wl)
+    out = mis.mis_score_labels(seg, dev(hid), dev(W), [3])
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 1)
