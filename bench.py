@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the MIS hot path on one MI355X.
+
+One step = the whole hot path over one batch already resident in HBM:
+``mis_build_segments`` (host checks, one metadata copy, builder kernels),
+``mis_attention_prefill`` (bf16 MFMA MIS attention) and ``mis_score_labels``
+(readout gather, LM head, split-vocab logsumexp, label log-probs).
+
+Default workload: one request with a 2048-token prefix and 64 items of 32
+tokens plus a closing delimiter; GQA 16 query / 8 KV heads, head_dim 128,
+bf16; label scoring with hidden 1024, vocabulary 151936, 2 labels. Inputs
+are seeded synthetic data shaped like the pages' workloads (one long shared
+prefix, tens to hundreds of short items).
+
+Prints one JSON line. ``value`` is the unmasked attention rate: 4*D*Hq
+times the number of (query, key) pairs the MIS mask lets through, divided by
+the attention kernel's average duration (HIP events on the launch stream).
+``item_scores_per_s`` is items divided by the whole step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MIS prefill attention TFLOP/s (unmasked) + item scores/sec, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4 SIMD x 1024 bf16 FLOP/clk x 2.4 GHz (dense MFMA)
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def visible_pairs(wl) -> int:
+    """(query, key) pairs the MIS mask allows, summed over requests (one head)."""
+    total = 0
+    lens = wl.item_lengths()
+    for r in range(wl.num_requests):
+        lq = int(wl.prefix_lens[r])
+        s = lens[int(wl.cu_items[r]) : int(wl.cu_items[r + 1])].astype(np.int64)
+        total += lq * (lq + 1) // 2 + int((s * lq + s * (s + 1) // 2).sum())
+    return total
+
+
+def attention_flops(wl) -> int:
+    return 4 * wl.d * wl.hq * visible_pairs(wl)
+
+
+def lm_head_cost(wl):
+    flops = 2 * wl.total_items * wl.hidden * wl.vocab
+    nbytes = 2 * (wl.vocab * wl.hidden + wl.total_items * wl.hidden) + 4 * wl.total_items * wl.num_labels
+    return flops, nbytes
+
+
+def _sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str, kernel_src: str):
+    """HBM bytes per launch from a committed counter summary, if it matches the kernel source."""
+    path = os.path.join(PROFILES, f"traffic_attention_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith("#"):
+                key, val = ln.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("source_sha256") != _sha(kernel_src):
+        return None
+    try:
+        return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, q, k, v, hid, W, labels, budget_s: float, flops: float):
+    """Time the fp64 oracle on a bounded sample of the same workload (host cores)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    so = oracle.build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts)
+    t_seg = time.perf_counter() - t0
+    # attention: dense explicit-mask rows cost the same for every row of a
+    # request, so time a random row sample and scale by T / rows
+    rng = np.random.default_rng(0)
+    T = wl.total_tokens
+    n_rows = 64
+    rows_done = 0
+    t_attn = 0.0
+    while rows_done < T:
+        rows = np.sort(rng.choice(T, size=min(n_rows, T), replace=False))
+        t1 = time.perf_counter()
+        oracle.attention(q, k, v, wl.cu_seqlens, so["item_id"], rows=rows)
+        t_attn += time.perf_counter() - t1
+        rows_done += len(rows)
+        if t_attn > budget_s * 0.6:
+            break
+        n_rows = min(T - rows_done, n_rows * 2) or 1
+    attn_full = t_attn * T / rows_done
+    t1 = time.perf_counter()
+    oracle.label_scores(hid, so["readout_pos"], W, labels)
+    t_score = time.perf_counter() - t1
+    total = t_seg + attn_full + t_score
+    return {
+        "value": flops / attn_full / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle (dense explicit-mask rows): segments and all "
+                   f"{wl.total_items} items' full-vocab label scores timed whole; attention "
+                   f"timed on {rows_done} of {T} query rows (all heads) and scaled by T/rows"),
+        "item_scores_per_s": wl.total_items / total,
+        "seconds_per_step": total,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import item_scoring_attention_amd as mis
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    wl = workloads.config(args.config)
+    if wl.dtype != "bf16":
+        print("bench.py times the bf16 path; pick a bf16 workload", file=sys.stderr)
+        return 2
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = workloads.qkv(wl)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    od = torch.empty_like(qd)
+    bm, bn = mis.mis_attention_tile_shape(mis.MIS_BF16, wl.hq, wl.hkv, wl.d)
+    seg_bytes = mis.mis_segments_bytes(wl.cu_seqlens, wl.total_items, bm, bn)
+    seg_buf = torch.empty(seg_bytes, dtype=torch.uint8, device="cuda")
+    seg = mis.mis_build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, bm, bn,
+                                 dev_buf=seg_buf)
+    has_score = wl.has_scoring
+    if has_score:
+        readout = seg.array("readout_pos").cpu().numpy()
+        hid = np.full((wl.total_tokens, wl.hidden), workloads.NAN_BF16, dtype=np.uint16)
+        hid[readout] = workloads.readout_values(wl)
+        hidd = dev(hid)
+        W = workloads.lm_head(wl)
+        Wd = dev(W)
+        labels = workloads.label_ids(wl)
+        scores = torch.empty((wl.total_items, wl.num_labels), dtype=torch.float32, device="cuda")
+        ws = torch.empty(mis.mis_score_workspace_bytes(wl.total_items, wl.vocab, wl.num_labels,
+                                                       wl.hidden, mis.MIS_BF16),
+                         dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = {name: [] for name in ("s0", "s1", "a1", "c1")}
+
+    def step(record: bool):
+        if record:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            ev["s0"].append(e)
+        s = mis.mis_build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, bm, bn,
+                                   dev_buf=seg_buf, stream=stream)
+        if record:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            ev["s1"].append(e)
+        mis.mis_attention_prefill(s, qd, kd, vd, o=od, stream=stream)
+        if record:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            ev["a1"].append(e)
+        if has_score:
+            mis.mis_score_labels(s, hidd, Wd, labels, scores=scores, ws=ws, stream=stream)
+        if record:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            ev["c1"].append(e)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    t_seg = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["s0"], ev["s1"])]))
+    t_att = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["s1"], ev["a1"])]))
+    t_sco = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["a1"], ev["c1"])]))
+    flops = attention_flops(wl)
+    tflops = flops / (t_att * 1e-3) / 1e12
+
+    attn_src = os.path.join(ROOT, "item_scoring_attention_amd", "csrc", "attn_bf16.hip")
+    traffic = read_traffic(wl.name, attn_src)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "item_scores_per_s": round(wl.total_items / (ms_step * 1e-3), 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "description": wl.description,
+            "requests": wl.num_requests,
+            "tokens": wl.total_tokens,
+            "items": wl.total_items,
+            "hq": wl.hq,
+            "hkv": wl.hkv,
+            "head_dim": wl.d,
+            "hidden": wl.hidden,
+            "vocab": wl.vocab,
+            "labels": wl.num_labels,
+            "tile": [bm, bn],
+            "seed": wl.seed,
+        },
+        "kernel_ms": {"segments": round(t_seg, 4), "attention": round(t_att, 4),
+                      "score": round(t_sco, 4)},
+        "roofline": {
+            "kernel": "attn_bf16_kernel (MIS attention)",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": flops,
+        },
+    }
+    if has_score:
+        f_lm, b_lm = lm_head_cost(wl)
+        t_bound = max(b_lm / (PEAK_HBM_GBS * 1e9), f_lm / (PEAK_BF16_TFLOPS * 1e12))
+        out["roofline_score"] = {
+            "kernel": "score_bf16_kernel + combine_kernel (LM head, split-vocab logsumexp)",
+            "bound": "hbm" if b_lm / (PEAK_HBM_GBS * 1e9) >= f_lm / (PEAK_BF16_TFLOPS * 1e12) else "mfma",
+            "achieved_gbs": round(b_lm / (t_sco * 1e-3) / 1e9, 1),
+            "achieved_tflops": round(f_lm / (t_sco * 1e-3) / 1e12, 2),
+            "frac": round(t_bound / (t_sco * 1e-3), 4),
+            "algorithmic_bytes_per_launch": b_lm,
+            "algorithmic_flops_per_launch": f_lm,
+        }
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": a.numel() * 2, "write": a.numel() * 2, "launches": 3}
+    if not args.no_cpu_baseline and has_score:
+        out["cpu_baseline"] = cpu_baseline(wl, q, k, v, hid, W, labels, args.cpu_budget, flops)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -40,6 +40,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int D = 128;
@@ -52,8 +53,13 @@ constexpr int VT_TILE = D * VT_LD;
 constexpr int STAGE = K_TILE + VT_TILE;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest allowed p
+// Fourth descriptor word of a raw (stride 0) buffer resource on CDNA: 32-bit
+// data format, so offsets are in bytes and out-of-range reads return zero.
+constexpr int kRsrcWord3 = 0x00020000;
 
 static_assert(BN == 64 && BM == 64, "kernel written for 64 x 64 tiles");
+
+__device__ constexpr bf16x2 kOnes2 = {__bf16(1.0f), __bf16(1.0f)};
 
 // Column of key kk (0..BN-1) in a V^T row: 4-key groups 1 and 2 of every
 // 16-key group swap places.
@@ -92,10 +98,11 @@ __global__ __launch_bounds__(128 * HG, 2) void attn_bf16_kernel(
   const int b_hi = (j1 + BN - 1) / BN;
   const int b_start = max(b_lo, a_end);
   const int n_visit = a_end + (b_hi - b_start);
-  const int8_t *cls_row = tile_class + cu_tiles[r] + qt * nkt;
+  const int cls_base = cu_tiles[r] + qt * nkt;  // tile_class index of key tile 0
+  const int32_t *cls_words = reinterpret_cast<const int32_t *>(tile_class);  // 256-byte aligned
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lane = tid & 63;
   const int g = lane >> 5;   // half-wave
   const int ql = lane & 31;  // query column owned by this lane
@@ -111,58 +118,63 @@ __global__ __launch_bounds__(128 * HG, 2) void attn_bf16_kernel(
   const int64_t kv_stride = int64_t(hkv) * D;
 
   // Q^T operand: 8 k-steps of 16 head dims, 8 consecutive dims per lane.
+  // Rows past the request end read as zeros (their outputs are not stored).
   bf16x8 qf[8];
   {
-    const __bf16 *qp = q + int64_t(base + j) * q_stride + int64_t(head) * D + 8 * g;
+    const uint32_t q_bytes = uint32_t(Tr) * uint32_t(q_stride) * 2u - uint32_t(head) * D * 2u;
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(q + int64_t(base) * q_stride + int64_t(head) * D), 0, q_bytes, kRsrcWord3);
+    const uint32_t qo = uint32_t(j) * uint32_t(q_stride) * 2u + 16u * g;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      if (row_ok) {
-        qf[kk] = *reinterpret_cast<const bf16x8 *>(qp + 16 * kk);
-      } else {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) qf[kk][s] = __bf16(0.f);
-      }
-    }
+    for (int kk = 0; kk < 8; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qo + 32u * kk, 0, 0));
   }
 
-  // Global -> register staging of one K/V tile.
+  // Global -> register staging of one K/V tile through raw buffer loads: the
+  // resources span exactly this request's rows of this KV head, so rows at or
+  // beyond the request end read as zeros without a branch.
   // K: 64 rows x 16 chunks of 8 dims = 1024 chunks; thread covers chunks tid + NT*i.
   // V: 16 groups of 4 keys x 16 groups of 8 dims = 256 blocks; thread covers tid + NT*i.
   constexpr int KCH = (BN * D / 8) / NT;
   constexpr int VBL = 256 / NT;
   uint4 kreg[KCH];
   uint4 vreg[VBL][4];
-  const __bf16 *kbase = k + int64_t(base) * kv_stride + int64_t(kvh) * D;
-  const __bf16 *vbase = v + int64_t(base) * kv_stride + int64_t(kvh) * D;
+  const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
+  const __bf16 *kreq = k + int64_t(base) * kv_stride + int64_t(kvh) * D;
+  const __bf16 *vreq = v + int64_t(base) * kv_stride + int64_t(kvh) * D;
+  uint32_t koff[KCH], voff[VBL];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int ch = tid + NT * i;
+    koff[i] = uint32_t(ch >> 4) * kv_row_bytes + uint32_t(ch & 15) * 16u;
+  }
+#pragma unroll
+  for (int i = 0; i < VBL; ++i) {
+    const int blk = tid + NT * i;
+    voff[i] = uint32_t(4 * (blk & 15)) * kv_row_bytes + uint32_t(blk >> 4) * 16u;
+  }
 
   auto tile_of = [&](int idx) { return idx < a_end ? idx : b_start + (idx - a_end); };
 
+  // The buffer range check covers only the per-lane offset, so each tile gets
+  // its own descriptor starting at its first key and ending at the request's
+  // last key of this KV head (k0 < Tr for every visited tile).
   auto load_tile = [&](int kt) {
     const int k0 = kt * BN;
+    const uint32_t nbytes = uint32_t(Tr - k0) * kv_row_bytes - uint32_t(kvh) * D * 2u;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(kreq + int64_t(k0) * kv_stride), 0, nbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(vreq + int64_t(k0) * kv_stride), 0, nbytes, kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch >> 4, col = (ch & 15) * 8;
-      if (k0 + row < Tr) {
-        kreg[i] = *reinterpret_cast<const uint4 *>(kbase + int64_t(k0 + row) * kv_stride + col);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
+    for (int i = 0; i < KCH; ++i)
+      kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], 0, 0));
 #pragma unroll
-    for (int i = 0; i < VBL; ++i) {
-      const int blk = tid + NT * i;
-      const int kg = blk & 15, dg = blk >> 4;
+    for (int i = 0; i < VBL; ++i)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = k0 + 4 * kg + rr;
-        if (key < Tr) {
-          vreg[i][rr] = *reinterpret_cast<const uint4 *>(vbase + int64_t(key) * kv_stride + 8 * dg);
-        } else {
-          vreg[i][rr] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
+      for (int rr = 0; rr < 4; ++rr)
+        vreg[i][rr] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[i] + uint32_t(rr) * kv_row_bytes, 0, 0));
   };
 
   auto store_tile = [&](int buf) {
@@ -205,10 +217,9 @@ __global__ __launch_bounds__(128 * HG, 2) void attn_bf16_kernel(
   float ms = -1e30f;  // running maximum in the scaled (log2) domain
   float lsum = 0.f;   // this lane's share of the row sum
 
-  if (n_visit > 0) {
-    load_tile(tile_of(0));
-    store_tile(0);
-  }
+  // Every query tile sees at least its diagonal key tile, so n_visit >= 1.
+  load_tile(tile_of(0));
+  store_tile(0);
   __syncthreads();
 
   for (int it = 0; it < n_visit; ++it) {
@@ -235,7 +246,8 @@ __global__ __launch_bounds__(128 * HG, 2) void attn_bf16_kernel(
     }
 
     // mask (partly visible tiles and the request's last key tile only)
-    const int cls = cls_row[kt];
+    const int ci = cls_base + kt;
+    const int cls = (cls_words[ci >> 2] >> (8 * (ci & 3))) & 0xff;
     const bool need_mask = (cls != 2) || (kt * BN + BN > Tr);
     if (need_mask) {
 #pragma unroll
@@ -244,7 +256,7 @@ __global__ __launch_bounds__(128 * HG, 2) void attn_bf16_kernel(
         for (int a = 0; a < 16; ++a) {
           const int key = kt * BN + 32 * b + 8 * (a >> 2) + 4 * g + (a & 3);
           const bool vis = key <= j && (key < lq || key >= jb);
-          if (!vis) sacc[b][a] = -INFINITY;
+          sacc[b][a] = vis ? sacc[b][a] : -INFINITY;
         }
     }
 
@@ -270,10 +282,15 @@ __global__ __launch_bounds__(128 * HG, 2) void attn_bf16_kernel(
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][a], c, -ms));
-        lsum += p;
-        pf[2 * b + (a >> 3)][a & 7] = __bf16(p);
+      for (int a = 0; a < 16; ++a)
+        pf[2 * b + (a >> 3)][a & 7] = __bf16(__builtin_amdgcn_exp2f(fmaf(sacc[b][a], c, -ms)));
+    // row sum of the bf16-rounded P (the values the PV product uses), two per dot2
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        bf16x2 pp = {pf[x][2 * y], pf[x][2 * y + 1]};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, lsum, false);
       }
 
     // O^T += V^T P^T over 4 steps of 16 keys
