@@ -31,7 +31,9 @@
  *   Every device write is enqueued on that stream; results are ready once the
  *   stream has been synchronised.
  * - The library never allocates device memory. The caller owns every device
- *   buffer; the *_bytes queries give the sizes.
+ *   buffer; the *_bytes queries give the sizes. mis_build_segments uploads its
+ *   metadata through a small ring of page-locked host slots that the library
+ *   allocates once per device and keeps until the process ends.
  * - Packed ("varlen") token-major layout: request r owns packed tokens
  *   [cu_seqlens[r], cu_seqlens[r+1]); its first prefix_lens[r] tokens are the
  *   prefix, then its items follow back to back in input order. Items are

@@ -38,7 +38,7 @@ _ERR_NAMES = {
     MIS_ERR_HIP: "MIS_ERR_HIP",
 }
 
-_i32p = ctypes.POINTER(ctypes.c_int32)
+_i32p = ctypes.c_void_p  # host int32 arrays are passed by address
 _i8p = ctypes.POINTER(ctypes.c_int8)
 
 
@@ -135,16 +135,19 @@ def _check(rc: int) -> None:
 
 
 def _host_i32(x) -> np.ndarray:
+    if isinstance(x, np.ndarray) and x.dtype == np.int32 and x.flags.c_contiguous:
+        return x
     a = np.ascontiguousarray(np.asarray(x, dtype=np.int64))
-    if a.size and (a.min() < np.iinfo(np.int32).min or a.max() > np.iinfo(np.int32).max):
+    if a.size and (a.min() < -(2**31) or a.max() > 2**31 - 1):
         raise ValueError("metadata value outside int32")
     return np.ascontiguousarray(a.astype(np.int32))
 
 
 def _ptr_i32(a: Optional[np.ndarray]):
-    if a is None:
+    """Address of a host int32 array (or None) for a ``const int32_t *`` parameter."""
+    if a is None or a.size == 0:
         return None
-    return a.ctypes.data_as(_i32p)
+    return a.ctypes.data
 
 
 def _torch():
@@ -245,8 +248,8 @@ def mis_build_segments(cu_seqlens, prefix_lens, cu_items, item_starts, block_m: 
         nbytes = mis_segments_bytes(cu, int(ci[-1]) if len(ci) else 0, block_m, block_n)
         dev_buf = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
     out = MisSegments()
-    _check(load().mis_build_segments(B, _ptr_i32(cu), _ptr_i32(pl), _ptr_i32(ci),
-                                     _ptr_i32(st) if st.size else None, int(block_m), int(block_n),
+    _check(load().mis_build_segments(B, _ptr_i32(cu), _ptr_i32(pl), _ptr_i32(ci), _ptr_i32(st),
+                                     int(block_m), int(block_n),
                                      ctypes.c_void_p(dev_buf.data_ptr()),
                                      dev_buf.numel() * dev_buf.element_size(), ctypes.byref(out),
                                      _stream(stream)))
@@ -260,8 +263,8 @@ def mis_attention_tile_shape(dtype, hq: int, hkv: int, head_dim: int):
     torch = _torch()
     code = dtype if isinstance(dtype, int) else (MIS_BF16 if dtype == torch.bfloat16 else MIS_F32)
     bm, bn = ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(load().mis_attention_tile_shape(code, int(hq), int(hkv), int(head_dim), ctypes.byref(bm),
-                                           ctypes.byref(bn)))
+    _check(load().mis_attention_tile_shape(code, int(hq), int(hkv), int(head_dim),
+                                           ctypes.addressof(bm), ctypes.addressof(bn)))
     return bm.value, bn.value
 
 
@@ -321,7 +324,7 @@ def mis_score_labels(seg: Segments, hidden, lm_head, label_ids: Sequence[int],
         ws = torch.empty(nbytes, dtype=torch.uint8, device=hidden.device)
     _check(load().mis_score_labels(ctypes.byref(seg.struct), _dev(hidden, "hidden"), H,
                                    _dev(lm_head, "lm_head"), V, _dtype_code(hidden),
-                                   _ptr_i32(lab) if lab.size else None, K, 1 if apply_softmax else 0,
+                                   _ptr_i32(lab), K, 1 if apply_softmax else 0,
                                    _dev(scores, "scores"), _dev(ws, "ws"),
                                    ws.numel() * ws.element_size(), _stream(stream)))
     return scores

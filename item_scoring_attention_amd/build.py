@@ -23,6 +23,11 @@ ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "segments.hip", "attn_f32.hip", "attn_bf16.hip", "score.hip"]
 
+# Per-source extra flags. The attention kernels keep their MFMA accumulators
+# in VGPRs: with the default heuristic the allocator parks them in AGPRs and
+# copies them back on every key tile.
+EXTRA_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 # -packed-fp32-ops keeps hipcc from forming packed fp32 VALU instructions.
 # The host pass warns that it does not know the feature; that is harmless.
 FLAGS = [
@@ -48,7 +53,7 @@ def _hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -74,6 +79,14 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
+    # A kernel template whose host-side instantiation fails leaves its launch
+    # stub undefined without a compile error; refuse such a library.
+    nm = shutil.which("nm")
+    if nm:
+        und = subprocess.run([nm, "-u", tmp], capture_output=True, text=True).stdout
+        bad = [ln.split()[-1] for ln in und.splitlines() if "__device_stub__" in ln]
+        if bad:
+            raise RuntimeError(f"undefined kernel launch stubs in {tmp}: {bad}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} in {time.time() - t0:.1f}s", flush=True)

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -35,6 +36,67 @@ int hip_fail(hipError_t e, const char *what) {
 }
 
 constexpr size_t kAlign = 256;
+
+// Pinned host staging for metadata uploads. A copy from pageable memory makes
+// the host wait for the stream, so the next launches could not be queued
+// ahead of the GPU. Each device gets a small ring of page-locked slots; a slot
+// is reused only after the event recorded behind its last copy has completed.
+// The slots live until the process ends (never freed: freeing during static
+// destruction could run after the HIP runtime has shut down).
+class StageRing {
+ public:
+  static constexpr int kSlots = 8;
+  static constexpr int kMaxDevices = 64;
+
+  // Copies `bytes` of `src` to `dst` (device) on `stream` through a pinned slot.
+  hipError_t upload(void *dst, const void *src, size_t bytes, hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu_);
+    Slot &s = slots_[dev][next_[dev]];
+    next_[dev] = (next_[dev] + 1) % kSlots;
+    if (!s.event) {
+      e = hipEventCreateWithFlags(&s.event, hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    } else if (s.busy) {
+      e = hipEventSynchronize(s.event);
+      if (e != hipSuccess) return e;
+    }
+    if (s.cap < bytes) {
+      if (s.host) hipHostFree(s.host);
+      s.host = nullptr;
+      s.cap = 0;
+      const size_t cap = std::max<size_t>(bytes, 64 * 1024);
+      e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+      if (e != hipSuccess) return e;
+      s.cap = cap;
+    }
+    std::memcpy(s.host, src, bytes);
+    e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(s.event, stream);
+    s.busy = (e == hipSuccess);
+    return e;
+  }
+
+ private:
+  struct Slot {
+    void *host = nullptr;
+    size_t cap = 0;
+    hipEvent_t event = nullptr;
+    bool busy = false;
+  };
+  std::mutex mu_;
+  Slot slots_[kMaxDevices][kSlots];
+  int next_[kMaxDevices] = {};
+};
+
+StageRing &stage_ring() {
+  static StageRing *ring = new StageRing();  // intentionally leaked
+  return *ring;
+}
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -246,9 +308,7 @@ int mis_build_segments(int32_t B, const int32_t *cu_seqlens_h, const int32_t *pr
   s.work = reinterpret_cast<const int32_t *>(base + L.work);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // Pageable source: the runtime stages it before returning, so the image
-  // may be released when this function returns.
-  hipError_t e = hipMemcpyAsync(dev_buf, img.data(), L.stage_end, hipMemcpyHostToDevice, st);
+  hipError_t e = stage_ring().upload(dev_buf, img.data(), L.stage_end, st);
   if (e != hipSuccess) return hip_fail(e, "staging segment metadata");
   e = mis::launch_segments(s, reinterpret_cast<const int32_t *>(base + L.item_starts), st);
   if (e != hipSuccess) return hip_fail(e, "segment builder launch");

@@ -325,6 +325,297 @@ __global__ __launch_bounds__(128 * HG, 2) void attn_bf16_kernel(
   }
 }
 
+// LDS-direct buffer load of 16 bytes per lane: lane l's bytes land at lds + 16*l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff,
+                                           0, 0, 0);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Two transposing 8-byte LDS reads (see the head-pair kernel's comment) joined
+// into one 8-key MFMA operand.
+__device__ __forceinline__ bf16x8 ds_read_vt(const char *p_lo, const char *p_hi) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p_lo);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p_hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// ---------------------------------------------------------------------------
+// DMA kernel. A wave owns 32 query tokens of HPW query heads (1 or 2) that
+// share a KV head; a workgroup is TB token blocks x HP wave columns, so it
+// covers BM = 32*TB tokens and HP*HPW query heads. With HPW = 2 every K or V
+// fragment read from LDS feeds two MFMAs (half the LDS traffic per FLOP) but
+// the wave needs the whole register file (one wave per SIMD); with HPW = 1 a
+// wave fits in half of it, two waves share each SIMD, and one wave's softmax
+// runs while the other's MFMAs execute.
+//
+// K and V tiles (64 keys x 128 dims, 16 KB each) go from HBM to LDS by buffer
+// loads with the LDS-direct form: a wave instruction writes 1 KB of LDS
+// contiguously (lane l at +16*l), so the layout is chosen by which global
+// 16-byte chunk each lane fetches. Both tiles are row-major [key][dim] with
+// 256-byte rows and an XOR swizzle of the 16-byte chunk index:
+//   K: chunk c of key r sits in slot c ^ (r & 15): the 16 consecutive keys
+//      that 16 lanes of one ds_read_b128 read at the same chunk land in 16
+//      different slots (all 64 banks);
+//   V: chunk c of key r sits in slot c ^ 4*(r & 3): the 4 keys x 4 chunks
+//      that 32 lanes of one ds_read_b64_tr_b16 read land in 16 different
+//      slots.
+// V^T fragments come from ds_read_b64_tr_b16: inside a 16-lane group, lanes
+// 4e..4e+3 read dims d0..d0+15 of key k0+e and lane i receives dim d0+i of
+// keys k0..k0+3. Two such reads give a lane the 8 keys {4g..4g+3,
+// 8+4g..8+4g+3} of a 16-key step that the S^T accumulator hands to P^T.
+template <int TB, int HP, int HPW>
+__global__ __launch_bounds__(64 * TB * HP, HPW == 1 ? 2 : 1) void attn_dma_kernel(
+    const int32_t *__restrict__ work, const int32_t *__restrict__ cu_seqlens,
+    const int32_t *__restrict__ prefix_lens, const int32_t *__restrict__ cu_tiles,
+    const int8_t *__restrict__ tile_class, const int32_t *__restrict__ item_id,
+    const int32_t *__restrict__ item_begin, const __bf16 *__restrict__ q,
+    const __bf16 *__restrict__ k, const __bf16 *__restrict__ v, __bf16 *__restrict__ o, int hq,
+    int hkv, float c /* softmax scale * log2(e) */) {
+  static_assert(HPW == 1 || HPW == 2, "one or two heads per wave");
+  constexpr int NW = TB * HP;             // waves
+  constexpr int BMT = 32 * TB;            // query tokens per workgroup
+  constexpr int TILE = BN * D;            // bf16 elements of one K or V tile
+  constexpr int ROWS_PER_WAVE = BN / NW;  // DMA rows per wave and tile
+  constexpr int DMA_PER_WAVE = ROWS_PER_WAVE / 4;
+  static_assert(BN % (4 * NW) == 0, "DMA split");
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[2][2][TILE];  // [stage][K, V]
+
+  const int gsz = hq / hkv;
+  const int groups = gsz / (HP * HPW);
+  const int kvh = blockIdx.x % hkv;
+  const int rest = blockIdx.x / hkv;
+  const int hc = rest % groups;
+  const int w = rest / groups;
+
+  const int r = work[4 * w + 0];
+  const int qt = work[4 * w + 1];
+  const int a_end = work[4 * w + 2];
+  const int b_lo = work[4 * w + 3];
+  const int base = cu_seqlens[r];
+  const int Tr = cu_seqlens[r + 1] - base;
+  const int lq = prefix_lens[r];
+  const int nkt = (Tr + BN - 1) / BN;
+  const int j1 = min(Tr, qt * BMT + BMT);
+  const int b_hi = (j1 + BN - 1) / BN;
+  const int b_start = max(b_lo, a_end);
+  const int n_visit = a_end + (b_hi - b_start);
+  const int cls_base = cu_tiles[r] + qt * nkt;
+  const int32_t *cls_words = reinterpret_cast<const int32_t *>(tile_class);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 5;
+  const int ql = lane & 31;
+  const int tb = wave % TB;
+  const int hp = wave / TB;
+  const int head0 = kvh * gsz + hc * HP * HPW + HPW * hp;  // heads head0 .. head0 + HPW - 1
+  const int j = qt * BMT + tb * 32 + ql;
+  const bool row_ok = j < Tr;
+  const int jb = (row_ok && j >= lq) ? item_begin[item_id[base + j]] - base : 0;
+
+  const int64_t q_stride = int64_t(hq) * D;
+  const int64_t kv_stride = int64_t(hkv) * D;
+  const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
+
+  // zero both V stages once: rows past the request end may be left unwritten
+  // by the DMA and must not hold NaN (0 * NaN in the PV product)
+  for (int i = tid; i < 2 * TILE / 8; i += 64 * NW) {
+    const int st = i / (TILE / 8), off = i % (TILE / 8);
+    *reinterpret_cast<uint4 *>(&smem[st][1][off * 8]) = make_uint4(0, 0, 0, 0);
+  }
+
+  // Q^T operands
+  bf16x8 qf[HPW][8];
+  {
+    const uint32_t q_bytes = uint32_t(Tr) * uint32_t(q_stride) * 2u - uint32_t(head0) * D * 2u;
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(q + int64_t(base) * q_stride + int64_t(head0) * D), 0, q_bytes, kRsrcWord3);
+    const uint32_t qo = uint32_t(j) * uint32_t(q_stride) * 2u + 16u * g;
+#pragma unroll
+    for (int h = 0; h < HPW; ++h)
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        qf[h][kk] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qo + 32u * kk + uint32_t(h) * D * 2u, 0, 0));
+  }
+
+  // DMA lane mapping: instruction i of this wave covers tile rows
+  // ROWS_PER_WAVE*wave + 4*i + (lane >> 4), LDS slot lane & 15.
+  uint32_t koff[DMA_PER_WAVE], voff[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int row = ROWS_PER_WAVE * wave + 4 * i + (lane >> 4);
+    const int slot = lane & 15;
+    koff[i] = uint32_t(row) * kv_row_bytes + 16u * uint32_t(slot ^ (row & 15));
+    voff[i] = uint32_t(row) * kv_row_bytes + 16u * uint32_t(slot ^ (4 * (row & 3)));
+  }
+  const __bf16 *kreq = k + int64_t(base) * kv_stride + int64_t(kvh) * D;
+  const __bf16 *vreq = v + int64_t(base) * kv_stride + int64_t(kvh) * D;
+  auto tile_of = [&](int idx) { return idx < a_end ? idx : b_start + (idx - a_end); };
+  // Each tile gets descriptors that start at its first key and end at the
+  // request's last key of this KV head, so rows past the end read as zero.
+  auto issue_tile = [&](int kt, int stage) {
+    const int k0 = kt * BN;
+    const uint32_t nbytes = uint32_t(Tr - k0) * kv_row_bytes - uint32_t(kvh) * D * 2u;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(kreq + int64_t(k0) * kv_stride), 0, nbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(vreq + int64_t(k0) * kv_stride), 0, nbytes, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      dma16(krs, &smem[stage][0][(ROWS_PER_WAVE * wave + 4 * i) * D], koff[i]);
+      dma16(vrs, &smem[stage][1][(ROWS_PER_WAVE * wave + 4 * i) * D], voff[i]);
+    }
+  };
+
+  // LDS read addresses (bytes within a tile).
+  // K: lane reads key 32*b + ql, chunk 2*kk + g -> slot (2*kk + g) ^ (ql & 15).
+  uint32_t kaddr[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) kaddr[kk] = uint32_t(ql) * 256u + 16u * uint32_t((2 * kk + g) ^ (ql & 15));
+  // V: 16-lane group G, e = (lane >> 2) & 3, qd = lane & 3: key 4*(G >> 1) + e (+16*ks, +8),
+  // dims 32*db + 16*(G & 1) + 4*qd -> chunk 4*db + 2*(G & 1) + (qd >> 1), half (qd & 1).
+  uint32_t vaddr[4];
+  {
+    const int G = lane >> 4, e = (lane >> 2) & 3, qd = lane & 3;
+    const int key = 4 * (G >> 1) + e;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int chunk = 4 * db + 2 * (G & 1) + (qd >> 1);
+      vaddr[db] = uint32_t(key) * 256u + 16u * uint32_t(chunk ^ (4 * (key & 3))) + 8u * uint32_t(qd & 1);
+    }
+  }
+
+  f32x16 oacc[HPW][4];
+#pragma unroll
+  for (int h = 0; h < HPW; ++h)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) oacc[h][db][a] = 0.f;
+  float ms[HPW], ls[HPW];
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+    ms[h] = -1e30f;
+    ls[h] = 0.f;
+  }
+
+  __syncthreads();  // V zero fill done before any DMA lands
+  issue_tile(tile_of(0), 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int it = 0; it < n_visit; ++it) {
+    const int kt = tile_of(it);
+    const int stage = it & 1;
+    if (it + 1 < n_visit) issue_tile(tile_of(it + 1), stage ^ 1);
+    const char *kb = reinterpret_cast<const char *>(smem[stage][0]);
+    const char *vb = reinterpret_cast<const char *>(smem[stage][1]);
+
+    // S^T = K Q^T over both 32-key blocks; each K fragment feeds HPW MFMAs
+    f32x16 sacc[HPW][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int h = 0; h < HPW; ++h)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) sacc[h][b][a] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + kaddr[kk] + 32 * 256 * b);
+#pragma unroll
+        for (int h = 0; h < HPW; ++h)
+          sacc[h][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[h][kk], sacc[h][b], 0, 0, 0);
+      }
+    }
+
+    const int ci = cls_base + kt;
+    const int cls = (cls_words[ci >> 2] >> (8 * (ci & 3))) & 0xff;
+    const bool need_mask = (cls != 2) || (kt * BN + BN > Tr);
+    if (need_mask) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int key = kt * BN + 32 * b + 8 * (a >> 2) + 4 * g + (a & 3);
+          const bool vis = key <= j && (key < lq || key >= jb);
+#pragma unroll
+          for (int h = 0; h < HPW; ++h) sacc[h][b][a] = vis ? sacc[h][b][a] : -INFINITY;
+        }
+    }
+
+    // online softmax per head -> P^T operands
+    bf16x8 pf[HPW][4];
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      float mx = sacc[h][0][0];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sacc[h][b][a]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mcand = mx * c;
+      const bool upd = mcand > ms[h] + kRescaleThreshold;
+      if (__any(upd)) {
+        const float alpha = upd ? __builtin_amdgcn_exp2f(ms[h] - mcand) : 1.0f;
+        ms[h] = upd ? mcand : ms[h];
+        ls[h] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) oacc[h][db][a] *= alpha;
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int a = 0; a < 16; ++a)
+          pf[h][2 * b + (a >> 3)][a & 7] = __bf16(__builtin_amdgcn_exp2f(fmaf(sacc[h][b][a], c, -ms[h])));
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          bf16x2 pp = {pf[h][x][2 * y], pf[h][x][2 * y + 1]};
+          ls[h] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls[h], false);
+        }
+    }
+
+    // O^T += V^T P^T; each V fragment feeds HPW MFMAs
+#pragma unroll
+    for (int ksx = 0; ksx < 4; ++ksx) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 vf = ds_read_vt(vb + vaddr[db] + ksx * 16 * 256, vb + vaddr[db] + ksx * 16 * 256 + 8 * 256);
+#pragma unroll
+        for (int h = 0; h < HPW; ++h)
+          oacc[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[h][ksx], oacc[h][db], 0, 0, 0);
+      }
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA for the next tile has landed
+    __syncthreads();                // ... and every wave's, and nobody reads this stage any more
+  }
+
+  if (row_ok) {
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      const float inv = 1.0f / (ls[h] + __shfl_xor(ls[h], 32));
+      __bf16 *op = o + int64_t(base + j) * q_stride + int64_t(head0 + h) * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = __bf16(oacc[h][db][4 * a4 + e] * inv);
+          *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * a4 + 4 * g) = ov;
+        }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const void *k,
@@ -337,16 +628,17 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
   const __bf16 *kp = static_cast<const __bf16 *>(k);
   const __bf16 *vp = static_cast<const __bf16 *>(v);
   __bf16 *op = static_cast<__bf16 *>(o);
-  if (gsz % 2 == 0) {
-    const int64_t blocks = int64_t(seg.num_work) * hkv * (gsz / 2);
+  int64_t blocks;
+  if (gsz % 2 == 0) {  // 2 token blocks x 2 heads, one head per wave, two waves per SIMD
+    blocks = int64_t(seg.num_work) * hkv * (gsz / 2);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    attn_bf16_kernel<2><<<dim3(unsigned(blocks)), 256, 0, st>>>(
+    attn_dma_kernel<2, 2, 1><<<dim3(unsigned(blocks)), 256, 0, st>>>(
         seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.item_id,
         seg.item_begin, qp, kp, vp, op, hq, hkv, c);
-  } else {
-    const int64_t blocks = int64_t(seg.num_work) * hkv * gsz;
+  } else {  // odd group size: 2 token blocks x 1 head
+    blocks = int64_t(seg.num_work) * hkv * gsz;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
-    attn_bf16_kernel<1><<<dim3(unsigned(blocks)), 128, 0, st>>>(
+    attn_dma_kernel<2, 1, 1><<<dim3(unsigned(blocks)), 128, 0, st>>>(
         seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.item_id,
         seg.item_begin, qp, kp, vp, op, hq, hkv, c);
   }

@@ -2,14 +2,16 @@
 // packing, the reused position-id rule and the Eq. 4 mask; items closed by a
 // delimiter token as in the LinkedIn SGLang blog's multi-item format).
 //
-// Three small kernels, stream-ordered:
+// One launch with three independent roles:
+//   tokens  one thread per token: item id (-1 = prefix) and position id
 //   items   one thread per item: absolute first token and readout position
 //           (the item's last token, its closing delimiter)
-//   tokens  one thread per token: item id (-1 = prefix) and position id
-//   tiles   one thread per block_m x block_n tile: class 0/1/2 from visible
-//           cell counts over in-range cells, counted row by row in closed
-//           form (segments are contiguous, so each row's visible keys are
-//           the prefix keys up to the row plus its own item's keys up to it)
+//   tiles   one thread per block_m x block_n tile: class 0/1/2 from the
+//           number of visible in-range cells. Segments are contiguous, so a
+//           row's visible keys are the prefix keys up to the row plus its own
+//           item's keys up to the row; the count over the rows of one
+//           segment is an arithmetic series, so a tile costs one step per
+//           segment it overlaps.
 #include "mis_internal.h"
 
 namespace mis {
@@ -35,51 +37,57 @@ __device__ __forceinline__ int request_of_item(const int32_t *cu_items, int B, i
   return lo;
 }
 
-__global__ void items_kernel(int B, int N, const int32_t *__restrict__ cu_seqlens,
-                             const int32_t *__restrict__ cu_items,
-                             const int32_t *__restrict__ item_starts, int32_t *__restrict__ item_begin,
-                             int32_t *__restrict__ readout_pos) {
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
-  const int r = request_of_item(cu_items, B, n);
-  const int32_t base = cu_seqlens[r];
-  const int32_t stop = (n + 1 < cu_items[r + 1]) ? item_starts[n + 1] : cu_seqlens[r + 1] - base;
-  item_begin[n] = base + item_starts[n];
-  readout_pos[n] = base + stop - 1;
+// Sum over a in [lo, hi] (inclusive) of max(0, min(a, k1) - m0).
+__device__ __forceinline__ int64_t sum_clip(int64_t lo, int64_t hi, int64_t m0, int64_t k1) {
+  int64_t total = 0;
+  const int64_t a1 = max(lo, m0 + 1), b1 = min(hi, k1);  // rising part: a - m0
+  if (b1 >= a1) total += (b1 - a1 + 1) * ((a1 - m0) + (b1 - m0)) / 2;
+  const int64_t a2 = max(lo, k1 + 1);  // flat part: k1 - m0
+  if (hi >= a2 && k1 > m0) total += (hi - a2 + 1) * (k1 - m0);
+  return total;
 }
 
-__global__ void tokens_kernel(int B, int T, const int32_t *__restrict__ cu_seqlens,
-                              const int32_t *__restrict__ prefix_lens,
-                              const int32_t *__restrict__ cu_items,
-                              const int32_t *__restrict__ item_starts, int32_t *__restrict__ item_id,
-                              int32_t *__restrict__ pos_id) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  const int r = last_le(cu_seqlens, B, t);
-  const int32_t u = t - cu_seqlens[r];
-  const int32_t lq = prefix_lens[r];
-  if (u < lq) {
-    item_id[t] = -1;
-    pos_id[t] = u;
+// One launch, three roles by block range: tokens, items, tiles. No role reads
+// another role's output, so they need no ordering.
+__global__ __launch_bounds__(256) void builder_kernel(
+    int B, int T, int N, int num_tiles, int bm, int bn, int tok_blocks, int item_blocks,
+    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ prefix_lens,
+    const int32_t *__restrict__ cu_items, const int32_t *__restrict__ item_starts,
+    const int32_t *__restrict__ cu_tiles, int32_t *__restrict__ item_id, int32_t *__restrict__ pos_id,
+    int32_t *__restrict__ item_begin, int32_t *__restrict__ readout_pos, int8_t *__restrict__ tile_class) {
+  const int blk = blockIdx.x;
+  if (blk < tok_blocks) {  // ---- per token: item id and reused position id
+    const int t = blk * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    const int r = last_le(cu_seqlens, B, t);
+    const int32_t u = t - cu_seqlens[r];
+    const int32_t lq = prefix_lens[r];
+    if (u < lq) {
+      item_id[t] = -1;
+      pos_id[t] = u;
+      return;
+    }
+    const int a = cu_items[r];
+    const int i = a + last_le(item_starts + a, cu_items[r + 1] - a, u);
+    item_id[t] = i;
+    pos_id[t] = lq + (u - item_starts[i]);
     return;
   }
-  const int a = cu_items[r];
-  const int i = a + last_le(item_starts + a, cu_items[r + 1] - a, u);
-  item_id[t] = i;
-  pos_id[t] = lq + (u - item_starts[i]);
-}
-
-__global__ void tiles_kernel(int B, int num_tiles, int bm, int bn,
-                             const int32_t *__restrict__ cu_seqlens,
-                             const int32_t *__restrict__ prefix_lens,
-                             const int32_t *__restrict__ cu_tiles,
-                             const int32_t *__restrict__ item_id,
-                             const int32_t *__restrict__ item_begin, int8_t *__restrict__ tile_class) {
-  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk < tok_blocks + item_blocks) {  // ---- per item: first token and readout token
+    const int n = (blk - tok_blocks) * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    const int r = request_of_item(cu_items, B, n);
+    const int32_t base = cu_seqlens[r];
+    const int32_t stop = (n + 1 < cu_items[r + 1]) ? item_starts[n + 1] : cu_seqlens[r + 1] - base;
+    item_begin[n] = base + item_starts[n];
+    readout_pos[n] = base + stop - 1;
+    return;
+  }
+  // ---- per tile: visible cells in closed form, segment by segment
+  const int g = (blk - tok_blocks - item_blocks) * blockDim.x + threadIdx.x;
   if (g >= num_tiles) return;
   const int r = last_le(cu_tiles, B, g);
-  const int32_t base = cu_seqlens[r];
-  const int32_t Tr = cu_seqlens[r + 1] - base;
+  const int32_t Tr = cu_seqlens[r + 1] - cu_seqlens[r];
   const int32_t lq = prefix_lens[r];
   const int32_t nkt = (Tr + bn - 1) / bn;
   const int32_t local = g - cu_tiles[r];
@@ -87,13 +95,18 @@ __global__ void tiles_kernel(int B, int num_tiles, int bm, int bn,
   const int32_t j0 = qt * bm, j1 = min(Tr, j0 + bm);
   const int32_t k0 = kt * bn, k1 = min(Tr, k0 + bn);
   int64_t visible = 0;
-  for (int32_t j = j0; j < j1; ++j) {
-    // prefix keys k < Lq with k <= j
-    const int32_t pe = min(min(lq, j + 1), k1);
-    visible += max(0, pe - k0);
-    if (j >= lq) {  // own-item keys in [begin of j's item, j]
-      const int32_t sb = item_begin[item_id[base + j]] - base;
-      visible += max(0, min(j + 1, k1) - max(sb, k0));
+  // prefix rows j in [j0, min(j1, Lq)): keys k in [k0, k1) with k <= j
+  if (j0 < lq) visible += sum_clip(j0 + 1, min(j1, lq), k0, k1);
+  // item rows: the prefix keys of the tile plus own-item keys up to the row
+  const int32_t r0 = max(j0, lq);
+  if (r0 < j1) {
+    const int a = cu_items[r], b = cu_items[r + 1];
+    const int64_t cp = max(0, min(k1, lq) - k0);
+    for (int i = a + last_le(item_starts + a, b - a, r0); i < b && item_starts[i] < j1; ++i) {
+      const int32_t s0 = item_starts[i];
+      const int32_t e0 = (i + 1 < b) ? item_starts[i + 1] : Tr;
+      const int32_t ra = max(s0, j0), rb = min(e0, j1);
+      visible += cp * (rb - ra) + sum_clip(ra + 1, rb, max(s0, k0), k1);
     }
   }
   const int64_t cells = int64_t(j1 - j0) * int64_t(k1 - k0);
@@ -103,19 +116,16 @@ __global__ void tiles_kernel(int B, int num_tiles, int bm, int bn,
 }  // namespace
 
 hipError_t launch_segments(const mis_segments &seg, const int32_t *item_starts, hipStream_t st) {
-  const int B = seg.num_requests, T = seg.total_tokens, N = seg.total_items;
   constexpr int kThreads = 256;
-  if (N > 0) {
-    items_kernel<<<(N + kThreads - 1) / kThreads, kThreads, 0, st>>>(
-        B, N, seg.cu_seqlens, seg.cu_items, item_starts, const_cast<int32_t *>(seg.item_begin),
-        const_cast<int32_t *>(seg.readout_pos));
-  }
-  tokens_kernel<<<(T + kThreads - 1) / kThreads, kThreads, 0, st>>>(
-      B, T, seg.cu_seqlens, seg.prefix_lens, seg.cu_items, item_starts,
-      const_cast<int32_t *>(seg.item_id), const_cast<int32_t *>(seg.pos_id));
-  tiles_kernel<<<(seg.num_tiles + kThreads - 1) / kThreads, kThreads, 0, st>>>(
-      B, seg.num_tiles, seg.block_m, seg.block_n, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles,
-      seg.item_id, seg.item_begin, const_cast<int8_t *>(seg.tile_class));
+  const int tok_blocks = (seg.total_tokens + kThreads - 1) / kThreads;
+  const int item_blocks = (seg.total_items + kThreads - 1) / kThreads;
+  const int tile_blocks = (seg.num_tiles + kThreads - 1) / kThreads;
+  builder_kernel<<<tok_blocks + item_blocks + tile_blocks, kThreads, 0, st>>>(
+      seg.num_requests, seg.total_tokens, seg.total_items, seg.num_tiles, seg.block_m, seg.block_n,
+      tok_blocks, item_blocks, seg.cu_seqlens, seg.prefix_lens, seg.cu_items, item_starts, seg.cu_tiles,
+      const_cast<int32_t *>(seg.item_id), const_cast<int32_t *>(seg.pos_id),
+      const_cast<int32_t *>(seg.item_begin), const_cast<int32_t *>(seg.readout_pos),
+      const_cast<int8_t *>(seg.tile_class));
   return hipGetLastError();
 }
 

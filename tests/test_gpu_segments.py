@@ -85,3 +85,25 @@ def test_segments_edge_shapes():
     ]
     for i, (p, it) in enumerate(cases):
         _check_segments(workloads.from_lengths(f"edge{i}", p, it, hq=8, hkv=4, d=128))
+
+
+def test_many_builds_in_flight_keep_their_own_metadata():
+    # more builds than staging slots, queued without a host sync in between
+    import item_scoring_attention_amd as mis
+
+    rng = np.random.default_rng(7)
+    wls, segs = [], []
+    for i in range(20):
+        lq = int(rng.integers(0, 400))
+        items = rng.integers(1, 60, size=int(rng.integers(1, 40))).tolist()
+        wl = workloads.from_lengths(f"q{i}", [lq], [items], hq=8, hkv=4, d=128)
+        bm, bn = mis.mis_attention_tile_shape(mis.MIS_BF16, 8, 4, 128)
+        segs.append(mis.mis_build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items,
+                                           wl.item_starts, bm, bn))
+        wls.append(wl)
+    for wl, seg in zip(wls, segs):
+        so = segments_oracle(wl)
+        assert np.array_equal(host(seg.array("item_id")), so["item_id"])
+        assert np.array_equal(host(seg.array("readout_pos")), so["readout_pos"])
+        cls, _ = oracle.tile_classes(wl.cu_seqlens, so["item_id"], seg.block_m, seg.block_n)
+        assert np.array_equal(host(seg.array("tile_class")), cls)
