@@ -26,6 +26,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int BV = kScoreBlockV;
+constexpr int kScoreStages = 3;  // LDS ring depth of the streaming kernel
 
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
@@ -154,20 +155,69 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(
 // ------------------------------------------------- bf16 streaming (N <= 64)
 // HBM-bound regime: every LM-head row is read once and feeds at most two
 // MFMAs per 16 hidden dims, so the kernel is a stream. 4 waves x 32 rows =
-// 128 vocabulary rows per workgroup. Each lane streams 64 contiguous bytes of
-// its row per 64-dim chunk, prefetched two chunks ahead; the gathered readout
-// rows of the chunk sit in LDS (double-buffered, shared by the 4 waves).
+// 128 vocabulary rows per workgroup; the hidden dimension is walked in
+// 64-dim chunks. Both operands of a chunk (128 W rows x 64 dims and the
+// gathered readout rows, items x 64 dims) go to an NS-deep LDS ring by
+// LDS-direct loads: 8 lanes cover one 128-byte line, so every load
+// instruction reads 8 whole lines. Chunk c + NS - 1 is issued while chunk c
+// is contracted. Past the last chunk the loads are still issued (W at an
+// out-of-range buffer offset, which returns zeros without a memory access;
+// X re-reading chunk 0) into a slot nobody reads, which keeps the loop free
+// of branches and every wait count constant.
+// LDS layout of a staged chunk: 128 bytes per row (W row or item), 16-byte
+// piece p of row r in slot p ^ ((r >> 1) & 7), so the 16 rows that 16 lanes
+// of one ds_read_b128 touch spread over all 64 banks.
 // K-slot order inside a chunk: k-step s of half-wave g covers dims
 // 32*g + 8*s .. +8 for both operands (any order works if A and B agree).
-template <int NI>
+__device__ __forceinline__ void lds_load16(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff,
+                                           0, 0, 0);
+}
+
+// s_waitcnt immediate: at most n vector-memory operations of this wave outstanding.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+
+// Workgroup barrier without the release/acquire fence of __syncthreads():
+// with LDS-direct loads in flight that fence waits for every outstanding
+// vector-memory operation, which would drain the ring. Callers order memory
+// themselves (s_waitcnt for their own LDS-direct loads; LDS reads of a slot
+// are consumed by MFMAs before the barrier that frees it).
+__device__ __forceinline__ void barrier_no_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Fourth descriptor word of a raw (stride 0) buffer resource: byte offsets,
+// out-of-range reads return zero.
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <int NI, int NS>
 __global__ __launch_bounds__(256) void score_stream_kernel(
     const __bf16 *__restrict__ hidden, const __bf16 *__restrict__ w, int H, int V, int N,
     const int32_t *__restrict__ readout_pos, LabelArgs labels, float *__restrict__ pmax,
     float *__restrict__ psum, float *__restrict__ plab, int nvt) {
-  constexpr int XP = 64 + 8;  // LDS row pitch (bf16) of a staged chunk: 144 B
-  constexpr int NIT = 32 * NI;  // items in the tile
-  __shared__ __attribute__((aligned(16))) __bf16 xs[2][NIT * XP];
-  __shared__ float red[4][NI][32];
+  static_assert(NI == 1 || NI == 2, "one or two item blocks");
+  constexpr int NIT = 32 * NI;                 // items in the tile
+  constexpr int WCH = BV * 64;                 // bf16 elements of a staged W chunk
+  constexpr int XCH = NIT * 64;                // ... and of a staged X chunk
+  constexpr int PER_CHUNK = BV / 32 + NI;      // vector-memory ops per wave per chunk
+  // One LDS object for the ring and the epilogue's exchange: with several
+  // __shared__ arrays the compiler tags each with an alias scope and makes
+  // every LDS read wait for the newest LDS-direct load into the same array.
+  struct Smem {
+    __bf16 w[NS][WCH];
+    __bf16 x[NS][XCH];
+    float red[4][NI][32];
+  };
+  __shared__ __attribute__((aligned(1024))) Smem sm;
+  auto &ws_ = sm.w;
+  auto &xs = sm.x;
+  auto &red = sm.red;
 
   const int vt = blockIdx.x;
   const int v0 = vt * BV;
@@ -175,14 +225,26 @@ __global__ __launch_bounds__(256) void score_stream_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 5, ql = lane & 31;
-  const int row = v0 + 32 * wave + ql;
-  const __bf16 *wrow = w + int64_t(min(row, V - 1)) * H + 32 * g;
+  const int piece = lane & 7;
 
-  // staging of the gathered rows: thread -> (item xi + 32*i, 16-byte chunk xc of the 64 dims)
-  const int xi = tid >> 3, xc = tid & 7;
-  static_assert(NI == 1 || NI == 2, "one or two item blocks");
-  const __bf16 *xrow0 = hidden + int64_t(readout_pos[min(xi, N - 1)]) * H + 8 * xc;
-  const __bf16 *xrow1 = hidden + int64_t(readout_pos[min(xi + 32, N - 1)]) * H + 8 * xc;
+  // W rows v0 .. v0 + 127 (rows past V read as zero). Instruction i of this
+  // wave stages rows 32*wave + 8*i .. +8 (lane >> 3 picks the row).
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16 *>(w + int64_t(v0) * H), 0, uint32_t(min(BV, V - v0)) * uint32_t(H) * 2u,
+      kRsrcWord3);
+  uint32_t woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * wave + 8 * i + (lane >> 3);
+    woff[i] = uint32_t(r) * uint32_t(H) * 2u + 16u * uint32_t(piece ^ ((r >> 1) & 7));
+  }
+  // Readout rows: instruction i of this wave stages items 32*i + 8*wave .. +8.
+  const __bf16 *xsrc[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int n = 32 * i + 8 * wave + (lane >> 3);
+    xsrc[i] = hidden + int64_t(readout_pos[min(n, N - 1)]) * H + 8 * (piece ^ ((n >> 1) & 7));
+  }
 
   f32x16 acc[NI];
 #pragma unroll
@@ -191,46 +253,51 @@ __global__ __launch_bounds__(256) void score_stream_kernel(
     for (int a = 0; a < 16; ++a) acc[ni][a] = 0.f;
 
   const int nch = H / 64;
-  bf16x8 wb0[4], wb1[4], wb2[4];  // prefetch ring of three chunks
-  auto load_w = [&](int c, bf16x8 (&dst)[4]) {
+  auto issue = [&](int c, int slot) {
+    const bool real = c < nch;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dst[s] = *reinterpret_cast<const bf16x8 *>(wrow + 64 * c + 8 * s);
-  };
-  uint4 xreg0 = make_uint4(0, 0, 0, 0), xreg1 = make_uint4(0, 0, 0, 0);
-  auto load_x = [&](int c) {
-    xreg0 = *reinterpret_cast<const uint4 *>(xrow0 + 64 * c);
-    if (NI > 1) xreg1 = *reinterpret_cast<const uint4 *>(xrow1 + 64 * c);
-  };
-  auto store_x = [&](int buf) {
-    *reinterpret_cast<uint4 *>(&xs[buf][xi * XP + 8 * xc]) = xreg0;
-    if (NI > 1) *reinterpret_cast<uint4 *>(&xs[buf][(xi + 32) * XP + 8 * xc]) = xreg1;
-  };
-  // chunk c: prefetch chunk c + 2 into `pre`, contract chunk c from `cur`
-  auto step = [&](int c, bf16x8 (&cur)[4], bf16x8 (&pre)[4]) {
-    if (c + 2 < nch) load_w(c + 2, pre);
-    if (c + 1 < nch) load_x(c + 1);
-    const __bf16 *xb = xs[c & 1];
+    for (int i = 0; i < 4; ++i)
+      lds_load16(wrs, &ws_[slot][(32 * wave + 8 * i) * 64], real ? woff[i] + 128u * uint32_t(c) : 0x80000000u);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(xb + (32 * ni + ql) * XP + 32 * g + 8 * s);
-        acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[s], bfr, acc[ni], 0, 0, 0);
-      }
-    if (c + 1 < nch) store_x((c + 1) & 1);
-    __syncthreads();
+    for (int i = 0; i < NI; ++i) lds_load16(xsrc[i] + (real ? 64 * c : 0), &xs[slot][(32 * i + 8 * wave) * 64]);
   };
 
-  load_w(0, wb0);
-  if (nch > 1) load_w(1, wb1);
-  load_x(0);
-  store_x(0);
-  __syncthreads();
-  for (int c = 0; c < nch; c += 3) {
-    step(c, wb0, wb2);
-    if (c + 1 < nch) step(c + 1, wb1, wb0);
-    if (c + 2 < nch) step(c + 2, wb2, wb1);
+  // LDS read offsets (elements) of this lane's fragments for k-step s.
+  const int wr = 32 * wave + ql;
+  int wrd[4], xrd[NI][4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    wrd[st] = wr * 64 + 8 * ((4 * g + st) ^ ((wr >> 1) & 7));
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int n = 32 * ni + ql;
+      xrd[ni][st] = n * 64 + 8 * ((4 * g + st) ^ ((n >> 1) & 7));
+    }
   }
+
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue(p, p);
+  int slot = 0;
+  for (int c = 0; c < nch; ++c) {
+    // chunk c landed: this wave's loads (NS - 2 chunks were issued after
+    // it), then everyone's; the slot chunk c - 1 used is free again.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * PER_CHUNK));
+    barrier_no_fence();
+    issue(c + NS - 1, slot == 0 ? NS - 1 : slot - 1);
+    const __bf16 *wb = ws_[slot];
+    const __bf16 *xb = xs[slot];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8 *>(wb + wrd[st]);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(xb + xrd[ni][st]);
+        acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[ni], 0, 0, 0);
+      }
+    }
+    slot = slot + 1 == NS ? 0 : slot + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing loads land before the workgroup ends
 
   // epilogue: element a of acc[ni] is z[row v0 + 32*wave + 8*(a/4) + 4*g + a%4][item 32*ni + ql]
   auto row_of = [&](int a) { return v0 + 32 * wave + 8 * (a >> 2) + 4 * g + (a & 3); };
@@ -388,11 +455,11 @@ hipError_t launch_score(const mis_segments &seg, const void *hidden, int H, cons
     const __bf16 *hp = static_cast<const __bf16 *>(hidden);
     const __bf16 *wp = static_cast<const __bf16 *>(lm_head);
     if (N <= 32 && H % 64 == 0) {
-      score_stream_kernel<1><<<nvt, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels, pmax,
-                                                 psum, plab, nvt);
+      score_stream_kernel<1, kScoreStages><<<nvt, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels,
+                                                               pmax, psum, plab, nvt);
     } else if (N <= 64 && H % 64 == 0) {
-      score_stream_kernel<2><<<nvt, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels, pmax,
-                                                 psum, plab, nvt);
+      score_stream_kernel<2, kScoreStages><<<nvt, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels,
+                                                               pmax, psum, plab, nvt);
     } else if (N <= 64) {
       score_bf16_kernel<1><<<dim3(nvt, (N + 63) / 64), 256, 0, st>>>(
           hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum, plab, nvt);
