@@ -26,11 +26,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int BV = kScoreBlockV;
-constexpr int kScoreStages = 3;  // LDS ring depth of the streaming kernel
 
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-// ---------------------------------------------------------------- bf16 MFMA
+// ------------------------------------------- bf16 MFMA, any H % 32 == 0
+// Operands straight from global memory (used when H is not a multiple of 64).
 // 4 waves: wv = wave & 1 picks 64 vocabulary rows, wn = wave >> 1 picks
 // 32*NI items. Workgroup tile: 128 rows x 64*NI items.
 template <int NI>
@@ -128,8 +128,8 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(
     for (int ni = 0; ni < NI; ++ni) {
       const int n = n0 + 32 * (NI * wn + ni) + ql;
       if (n < N) {
-        pmax[int64_t(n) * nvt + vt] = m[ni];
-        psum[int64_t(n) * nvt + vt] = red[0][wn][ni][ql] + red[1][wn][ni][ql];
+        pmax[int64_t(vt) * N + n] = m[ni];
+        psum[int64_t(vt) * N + n] = red[0][wn][ni][ql] + red[1][wn][ni][ql];
       }
     }
   }
@@ -152,11 +152,13 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(
   }
 }
 
-// ------------------------------------------------- bf16 streaming (N <= 64)
-// HBM-bound regime: every LM-head row is read once and feeds at most two
-// MFMAs per 16 hidden dims, so the kernel is a stream. 4 waves x 32 rows =
-// 128 vocabulary rows per workgroup; the hidden dimension is walked in
-// 64-dim chunks. Both operands of a chunk (128 W rows x 64 dims and the
+// ------------------------------------------ bf16 LDS-staged (H % 64 == 0)
+// Workgroup tile: 128 vocabulary rows x 32*NI items (4 waves x 32 rows, each
+// wave all the tile's items). With N <= 64 the kernel is a stream: every
+// LM-head row is read once and feeds at most two MFMAs per 16 hidden dims.
+// With more items the item tiles of one vocabulary tile run on one XCD and
+// re-read its W tile from L2; the tile then feeds NI MFMAs per fragment read.
+// The hidden dimension is walked in 64-dim chunks. Both operands of a chunk (128 W rows x 64 dims and the
 // gathered readout rows, items x 64 dims) go to an NS-deep LDS ring by
 // LDS-direct loads: 8 lanes cover one 128-byte line, so every load
 // instruction reads 8 whole lines. Chunk c + NS - 1 is issued while chunk c
@@ -197,11 +199,11 @@ __device__ __forceinline__ void barrier_no_fence() {
 constexpr int kRsrcWord3 = 0x00020000;
 
 template <int NI, int NS>
-__global__ __launch_bounds__(256) void score_stream_kernel(
+__global__ __launch_bounds__(256) void score_lds_kernel(
     const __bf16 *__restrict__ hidden, const __bf16 *__restrict__ w, int H, int V, int N,
     const int32_t *__restrict__ readout_pos, LabelArgs labels, float *__restrict__ pmax,
-    float *__restrict__ psum, float *__restrict__ plab, int nvt) {
-  static_assert(NI == 1 || NI == 2, "one or two item blocks");
+    float *__restrict__ psum, float *__restrict__ plab, int nvt, int nit) {
+  static_assert(NI == 1 || NI == 2 || NI == 4, "1, 2 or 4 item blocks of 32");
   constexpr int NIT = 32 * NI;                 // items in the tile
   constexpr int WCH = BV * 64;                 // bf16 elements of a staged W chunk
   constexpr int XCH = NIT * 64;                // ... and of a staged X chunk
@@ -219,7 +221,13 @@ __global__ __launch_bounds__(256) void score_stream_kernel(
   auto &xs = sm.x;
   auto &red = sm.red;
 
-  const int vt = blockIdx.x;
+  // Workgroup b runs on XCD b % 8 (round-robin dispatch). The nit item
+  // tiles of one vocabulary tile get consecutive workgroups of the same XCD,
+  // so its L2 serves the W tile to all of them.
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int vt = 8 * (jx / nit) + xcd;
+  const int n0 = (jx % nit) * NIT;
+  if (vt >= nvt) return;  // padding of the vocabulary tile count to a multiple of 8
   const int v0 = vt * BV;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int n = 32 * i + 8 * wave + (lane >> 3);
-    xsrc[i] = hidden + int64_t(readout_pos[min(n, N - 1)]) * H + 8 * (piece ^ ((n >> 1) & 7));
+    xsrc[i] = hidden + int64_t(readout_pos[min(n0 + n, N - 1)]) * H + 8 * (piece ^ ((n >> 1) & 7));
   }
 
   f32x16 acc[NI];
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing loads land before the workgroup ends
 
-  // epilogue: element a of acc[ni] is z[row v0 + 32*wave + 8*(a/4) + 4*g + a%4][item 32*ni + ql]
+  // epilogue: element a of acc[ni] is z[row v0 + 32*wave + 8*(a/4) + 4*g + a%4][item n0 + 32*ni + ql]
   auto row_of = [&](int a) { return v0 + 32 * wave + 8 * (a >> 2) + 4 * g + (a & 3); };
   float m[NI];
 #pragma unroll
@@ -329,10 +337,10 @@ __global__ __launch_bounds__(256) void score_stream_kernel(
   if (wave == 0 && g == 0) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      const int n = 32 * ni + ql;
+      const int n = n0 + 32 * ni + ql;
       if (n < N) {
-        pmax[int64_t(n) * nvt + vt] = m[ni];
-        psum[int64_t(n) * nvt + vt] = red[0][ni][ql] + red[1][ni][ql] + red[2][ni][ql] + red[3][ni][ql];
+        pmax[int64_t(vt) * N + n] = m[ni];
+        psum[int64_t(vt) * N + n] = red[0][ni][ql] + red[1][ni][ql] + red[2][ni][ql] + red[3][ni][ql];
       }
     }
   }
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(
       float z = 0.f;
 #pragma unroll
       for (int a = 0; a < 16; ++a) z = (a == at) ? acc[ni][a] : z;
-      const int n = 32 * ni + ql;
+      const int n = n0 + 32 * ni + ql;
       if (n < N) plab[int64_t(n) * labels.k + kx] = z;
     }
   }
@@ -382,8 +390,8 @@ __global__ __launch_bounds__(BV) void score_f32_kernel(
   if (tid == 0) {
     float t = 0.f;
     for (int i = 0; i < BV / 64; ++i) t += red[i];
-    pmax[int64_t(n) * nvt + vt] = m;
-    psum[int64_t(n) * nvt + vt] = t;
+    pmax[int64_t(vt) * N + n] = m;
+    psum[int64_t(vt) * N + n] = t;
   }
   if (ok)
     for (int kx = 0; kx < labels.k; ++kx)
@@ -412,12 +420,13 @@ __device__ __forceinline__ float block_sum(float x, float *sh) {
 
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ pmax,
                                                       const float *__restrict__ psum,
-                                                      const float *__restrict__ plab, int nvt, int K,
+                                                      const float *__restrict__ plab, int nvt, int N, int K,
                                                       int apply_softmax, float *__restrict__ out) {
   __shared__ float sh[4];
   const int n = blockIdx.x, tid = threadIdx.x;
-  const float *pm = pmax + int64_t(n) * nvt;
-  const float *ps = psum + int64_t(n) * nvt;
+  // partials are vocabulary-tile major: tile c of item n at c * N + n
+  const float *pm = pmax + n;
+  const float *ps = psum + n;
   const float *zl = plab + int64_t(n) * K;
   float *o = out + int64_t(n) * K;
   if (apply_softmax) {
@@ -431,10 +440,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     return;
   }
   float M = -INFINITY;
-  for (int c = tid; c < nvt; c += 256) M = fmaxf(M, pm[c]);
+  for (int c = tid; c < nvt; c += 256) M = fmaxf(M, pm[int64_t(c) * N]);
   M = block_max(M, sh);
   float s = 0.f;
-  for (int c = tid; c < nvt; c += 256) s += ps[c] * expf(pm[c] - M);
+  for (int c = tid; c < nvt; c += 256) s += ps[int64_t(c) * N] * expf(pm[int64_t(c) * N] - M);
   s = block_sum(s, sh);
   const float lse = M + logf(s);
   for (int kx = tid; kx < K; kx += 256) o[kx] = zl[kx] - lse;
@@ -454,12 +463,21 @@ hipError_t launch_score(const mis_segments &seg, const void *hidden, int H, cons
   if (dt == MIS_BF16) {
     const __bf16 *hp = static_cast<const __bf16 *>(hidden);
     const __bf16 *wp = static_cast<const __bf16 *>(lm_head);
-    if (N <= 32 && H % 64 == 0) {
-      score_stream_kernel<1, kScoreStages><<<nvt, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels,
-                                                               pmax, psum, plab, nvt);
-    } else if (N <= 64 && H % 64 == 0) {
-      score_stream_kernel<2, kScoreStages><<<nvt, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels,
-                                                               pmax, psum, plab, nvt);
+    if (H % 64 == 0) {
+      // 32, 64 or 128 items per workgroup; a 3-deep ring while W is streamed
+      // once (N <= 64), 2-deep (2 workgroups per CU) when item tiles reuse it
+      const int ni = N <= 32 ? 1 : N <= 64 ? 2 : 4;
+      const int nit = (N + 32 * ni - 1) / (32 * ni);
+      const unsigned grid = unsigned((nvt + 7) / 8 * 8 * nit);
+      if (ni == 1)
+        score_lds_kernel<1, 3><<<grid, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum,
+                                                     plab, nvt, nit);
+      else if (ni == 2)
+        score_lds_kernel<2, 3><<<grid, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum,
+                                                     plab, nvt, nit);
+      else
+        score_lds_kernel<4, 2><<<grid, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum,
+                                                     plab, nvt, nit);
     } else if (N <= 64) {
       score_bf16_kernel<1><<<dim3(nvt, (N + 63) / 64), 256, 0, st>>>(
           hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum, plab, nvt);
@@ -477,7 +495,7 @@ hipError_t launch_score(const mis_segments &seg, const void *hidden, int H, cons
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_kernel<<<N, 256, 0, st>>>(pmax, psum, plab, nvt, labels.k, apply_softmax, scores);
+  combine_kernel<<<N, 256, 0, st>>>(pmax, psum, plab, nvt, N, labels.k, apply_softmax, scores);
   return hipGetLastError();
 }
 
