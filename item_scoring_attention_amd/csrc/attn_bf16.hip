@@ -56,6 +56,7 @@
 // share it); the O rescale is skipped when no lane of the wave raised it.
 // Row sums add the bf16-rounded P (the values the PV product uses), two per
 // v_dot2_f32_bf16.
+#include "gfx950_util.h"
 #include "mis_internal.h"
 
 namespace mis {
@@ -72,23 +73,10 @@ constexpr int BM = kAttnBlockM;  // query tokens per workgroup
 constexpr int BN = kAttnBlockN;  // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 of the largest allowed p
-// Fourth descriptor word of a raw (stride 0) buffer resource on CDNA: 32-bit
-// data format, so offsets are in bytes and out-of-range reads return zero.
-constexpr int kRsrcWord3 = 0x00020000;
 
 static_assert(BN == 64 && BM == 64, "kernel written for 64 x 64 tiles");
 
 __device__ constexpr bf16x2 kOnes2 = {__bf16(1.0f), __bf16(1.0f)};
-
-// LDS-direct buffer load of 16 bytes per lane: lane l's bytes land at lds + 16*l.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff,
-                                           0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)p));
-}
 
 // The two transposing 8-byte reads of one V^T fragment: keys k0..k0+3 at
 // `addr`, keys k0+8..k0+11 eight rows (2048 bytes) further. The results are
@@ -108,6 +96,146 @@ template <int N>
 __device__ __forceinline__ bf16x8 vt_wait(s16x4 &lo, s16x4 &hi) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo), "+v"(hi) : "n"(N));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One 16-byte K fragment read (ds_read_b128 at addr + OFF) through inline
+// asm; like vt_read, the result is valid only after a frag_wait.
+template <int OFF>
+__device__ __forceinline__ void k_read(uint32_t addr, bf16x8 &f) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "n"(OFF) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void lgkm_wait(bf16x8 &f) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f) : "n"(N));
+}
+
+// Wait for fragment f of an asm-read pipeline: n reads were issued after it.
+__device__ __forceinline__ void frag_wait(bf16x8 &f, int n) {
+  switch (n) {
+    case 0: lgkm_wait<0>(f); break;
+    case 1: lgkm_wait<1>(f); break;
+    case 2: lgkm_wait<2>(f); break;
+    case 3: lgkm_wait<3>(f); break;
+    case 4: lgkm_wait<4>(f); break;
+    case 5: lgkm_wait<5>(f); break;
+    case 6: lgkm_wait<6>(f); break;
+    case 7: lgkm_wait<7>(f); break;
+    default: lgkm_wait<8>(f); break;
+  }
+}
+
+// V^T fragment through vt_read, returned in one register quad once n reads
+// issued after it may still be outstanding.
+__device__ __forceinline__ bf16x8 vt_take(s16x4 &lo, s16x4 &hi, int n) {
+  switch (n) {
+    case 0: return vt_wait<0>(lo, hi);
+    case 2: return vt_wait<2>(lo, hi);
+    case 4: return vt_wait<4>(lo, hi);
+    case 6: return vt_wait<6>(lo, hi);
+    default: return vt_wait<8>(lo, hi);
+  }
+}
+
+// Fragment reads run KD fragments ahead of the MFMAs that use them.
+constexpr int KD = 4;
+
+// S^T (64 keys x 32 queries, two accumulators) of the K tile at LDS byte
+// offset kb. Fragment f covers dims 16*(f/2) .. +16 of key block f%2; the
+// lane reads key 32*(f%2) + l%32 at the swizzled slot kaddr[f/2].
+__device__ __forceinline__ void qk_tile(uint32_t kb, const uint32_t (&kaddr)[8], const bf16x8 (&qf)[8],
+                                        f32x16 (&sacc)[2]) {
+  bf16x8 kf[KD + 1];
+  auto kread = [&](int f) {
+    if (f & 1)
+      k_read<32 * 256>(kb + kaddr[f >> 1], kf[f % (KD + 1)]);
+    else
+      k_read<0>(kb + kaddr[f >> 1], kf[f % (KD + 1)]);
+  };
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int a = 0; a < 16; ++a) sacc[b][a] = 0.f;
+#pragma unroll
+  for (int f = 0; f < KD; ++f) kread(f);
+#pragma unroll
+  for (int f = 0; f < 16; ++f) {
+    if (f + KD < 16) kread(f + KD);
+    frag_wait(kf[f % (KD + 1)], min(KD, 15 - f));
+    sacc[f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[f % (KD + 1)], qf[f >> 1], sacc[f & 1], 0, 0, 0);
+  }
+}
+
+// O^T += V^T P^T over the V tile at LDS byte offset vb: 16 steps, ks = step/4
+// picks 16 keys, db = step%4 picks 32 dims.
+__device__ __forceinline__ void pv_tile(uint32_t vb, const uint32_t (&vaddr)[4], const bf16x8 (&pf)[4],
+                                        f32x16 (&oacc)[4]) {
+  s16x4 lo[KD + 1], hi[KD + 1];
+  auto vread = [&](int step) {
+    vt_read(vb + vaddr[step & 3] + (step >> 2) * 16 * 256, lo[step % (KD + 1)], hi[step % (KD + 1)]);
+  };
+#pragma unroll
+  for (int step = 0; step < KD; ++step) vread(step);
+#pragma unroll
+  for (int step = 0; step < 16; ++step) {
+    if (step + KD < 16) vread(step + KD);
+    const bf16x8 vf = vt_take(lo[step % (KD + 1)], hi[step % (KD + 1)], 2 * min(KD, 15 - step));
+    oacc[step & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[step >> 2], oacc[step & 3], 0, 0, 0);
+  }
+}
+
+// Eq. 4 mask of key tile kt for this lane's query row j (prefix keys up to
+// j; for an item row also its own item's keys from jb on); out-of-range and
+// invisible cells become -inf.
+__device__ __forceinline__ void mask_tile(f32x16 (&sacc)[2], int kt, int g, int j, int lq, int jb) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const int key = kt * BN + 32 * b + 8 * (a >> 2) + 4 * g + (a & 3);
+      const bool vis = key <= j && (key < lq || key >= jb);
+      sacc[b][a] = vis ? sacc[b][a] : -INFINITY;
+    }
+}
+
+// Online softmax of one S^T tile (exp2 domain, c = scale * log2 e): raises
+// the running maximum ms lazily, rescales O and the two partial row sums when
+// it does, and leaves P^T (bf16) in pf. Max and sums use independent chains.
+__device__ __forceinline__ void softmax_tile(const f32x16 (&sacc)[2], float c, float &ms, float (&ls)[2],
+                                             f32x16 (&oacc)[4], bf16x8 (&pf)[4]) {
+  float m4[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) m4[t] = fmaxf(sacc[t >> 1][8 * (t & 1)], sacc[t >> 1][8 * (t & 1) + 1]);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int a = 2; a < 8; ++a) m4[t] = fmaxf(m4[t], sacc[t >> 1][8 * (t & 1) + a]);
+  float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mcand = mx * c;
+  const bool upd = mcand > ms + kRescaleThreshold;
+  if (__any(upd)) {
+    const float alpha = upd ? __builtin_amdgcn_exp2f(ms - mcand) : 1.0f;
+    ms = upd ? mcand : ms;
+    ls[0] *= alpha;
+    ls[1] *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) oacc[db][a] *= alpha;
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int a = 0; a < 16; ++a)
+      pf[2 * b + (a >> 3)][a & 7] = __bf16(__builtin_amdgcn_exp2f(fmaf(sacc[b][a], c, -ms)));
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      bf16x2 pp = {pf[x][2 * y], pf[x][2 * y + 1]};
+      ls[y & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls[y & 1], false);
+    }
 }
 
 template <int TB, int HP>
@@ -196,23 +324,6 @@ __global__ __launch_bounds__(64 * TB * HP, 2) void attn_dma_kernel(
   const __bf16 *kreq = k + int64_t(base) * kv_stride + int64_t(kvh) * D;
   const __bf16 *vreq = v + int64_t(base) * kv_stride + int64_t(kvh) * D;
   auto tile_of = [&](int idx) { return idx < a_end ? idx : b_start + (idx - a_end); };
-  // Each tile gets descriptors that start at its first key and end at the
-  // request's last key of this KV head, so rows past the end read as zero
-  // (the range check covers only the per-lane offset).
-  auto issue_tile = [&](int kt, int stage) {
-    const int k0 = kt * BN;
-    const uint32_t nbytes = uint32_t(Tr - k0) * kv_row_bytes - uint32_t(kvh) * D * 2u;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16 *>(kreq + int64_t(k0) * kv_stride), 0, nbytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16 *>(vreq + int64_t(k0) * kv_stride), 0, nbytes, kRsrcWord3);
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      dma16(krs, &smem[stage][0][(ROWS_PER_WAVE * wave + 4 * i) * D], koff[i]);
-      dma16(vrs, &smem[stage][1][(ROWS_PER_WAVE * wave + 4 * i) * D], voff[i]);
-    }
-  };
-
   // LDS read addresses (bytes within a tile).
   // K: lane reads key 32*b + ql, chunk 2*kk + g -> slot (2*kk + g) ^ (ql & 15).
   uint32_t kaddr[8];
@@ -236,7 +347,24 @@ __global__ __launch_bounds__(64 * TB * HP, 2) void attn_dma_kernel(
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int a = 0; a < 16; ++a) oacc[db][a] = 0.f;
-  float ms = -1e30f, ls = 0.f;
+  float ms = -1e30f, ls[2] = {0.f, 0.f};
+
+  // Each tile gets descriptors that start at its first key and end at the
+  // request's last key of this KV head, so rows past the end read as zero
+  // (the range check covers only the per-lane offset).
+  auto issue_tile = [&](int kt, int stage) {
+    const int k0 = kt * BN;
+    const uint32_t nbytes = uint32_t(Tr - k0) * kv_row_bytes - uint32_t(kvh) * D * 2u;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(kreq + int64_t(k0) * kv_stride), 0, nbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(vreq + int64_t(k0) * kv_stride), 0, nbytes, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      lds_load16(krs, &smem[stage][0][(ROWS_PER_WAVE * wave + 4 * i) * D], koff[i]);
+      lds_load16(vrs, &smem[stage][1][(ROWS_PER_WAVE * wave + 4 * i) * D], voff[i]);
+    }
+  };
 
   __syncthreads();  // V zero fill done before any DMA lands
   issue_tile(tile_of(0), 0);
@@ -247,100 +375,21 @@ __global__ __launch_bounds__(64 * TB * HP, 2) void attn_dma_kernel(
     const int kt = tile_of(it);
     const int stage = it & 1;
     if (it + 1 < n_visit) issue_tile(tile_of(it + 1), stage ^ 1);
-    const char *kb = reinterpret_cast<const char *>(smem[stage][0]);
-    const uint32_t vb = lds_addr(smem[stage][1]);
-
-    // S^T = K Q^T over both 32-key blocks
     f32x16 sacc[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int a = 0; a < 16; ++a) sacc[b][a] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + kaddr[kk] + 32 * 256 * b);
-        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[b], 0, 0, 0);
-      }
-    }
-
+    qk_tile(lds_addr(smem[stage][0]), kaddr, qf, sacc);
     const int ci = cls_base + kt;
     const int cls = (cls_words[ci >> 2] >> (8 * (ci & 3))) & 0xff;
-    const bool need_mask = (cls != 2) || (kt * BN + BN > Tr);
-    if (need_mask) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int key = kt * BN + 32 * b + 8 * (a >> 2) + 4 * g + (a & 3);
-          const bool vis = key <= j && (key < lq || key >= jb);
-          sacc[b][a] = vis ? sacc[b][a] : -INFINITY;
-        }
-    }
-
-    // online softmax -> P^T operands
+    if ((cls != 2) || (kt * BN + BN > Tr)) mask_tile(sacc, kt, g, j, lq, jb);
     bf16x8 pf[4];
-    {
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sacc[b][a]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mcand = mx * c;
-      const bool upd = mcand > ms + kRescaleThreshold;
-      if (__any(upd)) {
-        const float alpha = upd ? __builtin_amdgcn_exp2f(ms - mcand) : 1.0f;
-        ms = upd ? mcand : ms;
-        ls *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int a = 0; a < 16; ++a) oacc[db][a] *= alpha;
-      }
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int a = 0; a < 16; ++a)
-          pf[2 * b + (a >> 3)][a & 7] = __bf16(__builtin_amdgcn_exp2f(fmaf(sacc[b][a], c, -ms)));
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          bf16x2 pp = {pf[x][2 * y], pf[x][2 * y + 1]};
-          ls = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, ls, false);
-        }
-    }
-
-    // O^T += V^T P^T in 16 steps (ks = step / 4 picks 16 keys, db = step % 4
-    // picks 32 dims). The fragment of step s + 2 is requested before step s's
-    // MFMA; the wait leaves the reads of steps s + 1 and s + 2 in flight.
-    {
-      s16x4 lo[3], hi[3];
-      auto vread = [&](int step) {
-        vt_read(vb + vaddr[step & 3] + (step >> 2) * 16 * 256, lo[step % 3], hi[step % 3]);
-      };
-      vread(0);
-      vread(1);
-#pragma unroll
-      for (int step = 0; step < 16; ++step) {
-        if (step + 2 < 16) vread(step + 2);
-        bf16x8 vf;
-        if (step < 14)
-          vf = vt_wait<4>(lo[step % 3], hi[step % 3]);
-        else if (step == 14)
-          vf = vt_wait<2>(lo[step % 3], hi[step % 3]);
-        else
-          vf = vt_wait<0>(lo[step % 3], hi[step % 3]);
-        oacc[step & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[step >> 2], oacc[step & 3], 0, 0, 0);
-      }
-    }
-
+    softmax_tile(sacc, c, ms, ls, oacc, pf);
+    pv_tile(lds_addr(smem[stage][1]), vaddr, pf, oacc);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA for the next tile has landed
     __syncthreads();                // ... and every wave's, and nobody reads this stage any more
   }
 
   if (row_ok) {
-    const float inv = 1.0f / (ls + __shfl_xor(ls, 32));
+    const float lsum = ls[0] + ls[1];
+    const float inv = 1.0f / (lsum + __shfl_xor(lsum, 32));
     __bf16 *op = o + int64_t(base + j) * q_stride + int64_t(head) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)

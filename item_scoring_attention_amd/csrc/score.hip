@@ -16,6 +16,7 @@
 // Pass 2 (one wave per item): merge the partials exactly,
 // lse = M + log(sum_c s_c * exp(m_c - M)), and write z_label - lse (or the
 // softmax over the label logits).
+#include "gfx950_util.h"
 #include "mis_internal.h"
 
 namespace mis {
@@ -171,33 +172,6 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(
 // of one ds_read_b128 touch spread over all 64 banks.
 // K-slot order inside a chunk: k-step s of half-wave g covers dims
 // 32*g + 8*s .. +8 for both operands (any order works if A and B agree).
-__device__ __forceinline__ void lds_load16(const void *src, void *lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-}
-
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff,
-                                           0, 0, 0);
-}
-
-// s_waitcnt immediate: at most n vector-memory operations of this wave outstanding.
-constexpr int waitcnt_vm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
-
-// Workgroup barrier without the release/acquire fence of __syncthreads():
-// with LDS-direct loads in flight that fence waits for every outstanding
-// vector-memory operation, which would drain the ring. Callers order memory
-// themselves (s_waitcnt for their own LDS-direct loads; LDS reads of a slot
-// are consumed by MFMAs before the barrier that frees it).
-__device__ __forceinline__ void barrier_no_fence() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Fourth descriptor word of a raw (stride 0) buffer resource: byte offsets,
-// out-of-range reads return zero.
-constexpr int kRsrcWord3 = 0x00020000;
-
 template <int NI, int NS>
 __global__ __launch_bounds__(256) void score_lds_kernel(
     const __bf16 *__restrict__ hidden, const __bf16 *__restrict__ w, int H, int V, int N,
