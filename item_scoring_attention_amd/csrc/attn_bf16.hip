@@ -11,8 +11,11 @@
 // Work decomposition
 //   A workgroup takes one 64-token query tile, one KV head and HP query heads
 //   of that KV head: TB = 2 token blocks x HP heads, one wave per (32 query
-//   tokens, head). A wave needs ~210 VGPRs, so two waves share each SIMD and
-//   one wave's softmax runs beside the other's MFMAs. The workgroup order
+//   tokens, head). A wave needs ~180 VGPRs, so two waves share each SIMD and
+//   one wave's softmax runs beside the other's MFMAs: HP = 2 runs two
+//   workgroups per CU, HP = 4 (GQA groups of 4 or more, enough work) one
+//   workgroup of 8 waves that shares each staged K/V tile among 4 heads, and
+//   HP = 1 serves odd group sizes. The workgroup order
 //   puts the KV head in the fastest-varying position, so with 8 KV heads
 //   every XCD (workgroups are dealt round-robin to the 8 XCDs) serves one KV
 //   head and its K/V stay in that XCD's L2. Query tiles arrive longest first
@@ -403,6 +406,19 @@ __global__ __launch_bounds__(64 * TB * HP, 2) void attn_dma_kernel(
   }
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <int TB, int HP>
 hipError_t launch_variant(const mis_segments &seg, const __bf16 *qp, const __bf16 *kp, const __bf16 *vp,
                           __bf16 *op, int hq, int hkv, float c, hipStream_t st) {
@@ -426,6 +442,11 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
   const __bf16 *kp = static_cast<const __bf16 *>(k);
   const __bf16 *vp = static_cast<const __bf16 *>(v);
   __bf16 *op = static_cast<__bf16 *>(o);
+  // 4 heads per workgroup (8 waves, one workgroup per CU) halve the K/V
+  // staging per FLOP but leave half as many workgroups to balance: taken only
+  // when every CU still gets at least 8 of them.
+  if (gsz % 4 == 0 && int64_t(seg.num_work) * (hq / 4) >= 8 * int64_t(device_cus()))
+    return launch_variant<2, 4>(seg, qp, kp, vp, op, hq, hkv, c, st);
   if (gsz % 2 == 0)  // 2 token blocks x 2 heads of one KV head
     return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, st);
   return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, st);  // odd group size
