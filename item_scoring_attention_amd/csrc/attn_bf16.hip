@@ -59,6 +59,8 @@
 // share it); the O rescale is skipped when no lane of the wave raised it.
 // Row sums add the bf16-rounded P (the values the PV product uses), two per
 // v_dot2_f32_bf16.
+#include <utility>
+
 #include "gfx950_util.h"
 #include "mis_internal.h"
 
@@ -82,13 +84,26 @@ static_assert(BN == 64 && BM == 64, "kernel written for 64 x 64 tiles");
 __device__ constexpr bf16x2 kOnes2 = {__bf16(1.0f), __bf16(1.0f)};
 
 // The two transposing 8-byte reads of one V^T fragment: keys k0..k0+3 at
-// `addr`, keys k0+8..k0+11 eight rows (2048 bytes) further. The results are
-// not ready when the asm ends: vt_wait<N> must come before any use.
+// addr + OFF, keys k0+8..k0+11 eight rows (2048 bytes) further. The results
+// are not ready when the asm ends: vt_wait<N> must come before any use.
+template <int OFF>
 __device__ __forceinline__ void vt_read(uint32_t addr, s16x4 &lo, s16x4 &hi) {
-  asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:2048"
+  static_assert(OFF >= 0 && OFF + 2048 < 65536, "DS offset field");
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
                : "=&v"(lo), "=v"(hi)
-               : "v"(addr)
+               : "v"(addr), "n"(OFF), "n"(OFF + 2048)
                : "memory");
+}
+
+// f(std::integral_constant<int, I>) for I = 0 .. N-1, so that I can feed
+// template arguments (immediate offsets and wait counts).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Wait until at most N LDS operations of this wave are outstanding. LDS
@@ -105,6 +120,7 @@ __device__ __forceinline__ bf16x8 vt_wait(s16x4 &lo, s16x4 &hi) {
 // asm; like vt_read, the result is valid only after a frag_wait.
 template <int OFF>
 __device__ __forceinline__ void k_read(uint32_t addr, bf16x8 &f) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offset field");
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "n"(OFF) : "memory");
 }
 
@@ -113,78 +129,50 @@ __device__ __forceinline__ void lgkm_wait(bf16x8 &f) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f) : "n"(N));
 }
 
-// Wait for fragment f of an asm-read pipeline: n reads were issued after it.
-__device__ __forceinline__ void frag_wait(bf16x8 &f, int n) {
-  switch (n) {
-    case 0: lgkm_wait<0>(f); break;
-    case 1: lgkm_wait<1>(f); break;
-    case 2: lgkm_wait<2>(f); break;
-    case 3: lgkm_wait<3>(f); break;
-    case 4: lgkm_wait<4>(f); break;
-    case 5: lgkm_wait<5>(f); break;
-    case 6: lgkm_wait<6>(f); break;
-    case 7: lgkm_wait<7>(f); break;
-    default: lgkm_wait<8>(f); break;
-  }
-}
-
-// V^T fragment through vt_read, returned in one register quad once n reads
-// issued after it may still be outstanding.
-__device__ __forceinline__ bf16x8 vt_take(s16x4 &lo, s16x4 &hi, int n) {
-  switch (n) {
-    case 0: return vt_wait<0>(lo, hi);
-    case 2: return vt_wait<2>(lo, hi);
-    case 4: return vt_wait<4>(lo, hi);
-    case 6: return vt_wait<6>(lo, hi);
-    default: return vt_wait<8>(lo, hi);
-  }
-}
-
 // Fragment reads run KD fragments ahead of the MFMAs that use them.
 constexpr int KD = 4;
 
 // S^T (64 keys x 32 queries, two accumulators) of the K tile at LDS byte
-// offset kb. Fragment f covers dims 16*(f/2) .. +16 of key block f%2; the
-// lane reads key 32*(f%2) + l%32 at the swizzled slot kaddr[f/2].
-__device__ __forceinline__ void qk_tile(uint32_t kb, const uint32_t (&kaddr)[8], const bf16x8 (&qf)[8],
-                                        f32x16 (&sacc)[2]) {
+// offset KOFF. Fragment f covers dims 16*(f/2) .. +16 of key block f%2; the
+// lane reads key 32*(f%2) + l%32 at the swizzled address kaddr[f/2]
+// (absolute LDS address of that slot in a tile at offset 0).
+template <int KOFF>
+__device__ __forceinline__ void qk_tile(const uint32_t (&kaddr)[8], const bf16x8 (&qf)[8], f32x16 (&sacc)[2]) {
   bf16x8 kf[KD + 1];
-  auto kread = [&](int f) {
-    if (f & 1)
-      k_read<32 * 256>(kb + kaddr[f >> 1], kf[f % (KD + 1)]);
-    else
-      k_read<0>(kb + kaddr[f >> 1], kf[f % (KD + 1)]);
+  auto kread = [&](auto fc) {
+    constexpr int f = decltype(fc)::value;
+    k_read<KOFF + (f & 1) * 32 * 256>(kaddr[f >> 1], kf[f % (KD + 1)]);
   };
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int a = 0; a < 16; ++a) sacc[b][a] = 0.f;
-#pragma unroll
-  for (int f = 0; f < KD; ++f) kread(f);
-#pragma unroll
-  for (int f = 0; f < 16; ++f) {
-    if (f + KD < 16) kread(f + KD);
-    frag_wait(kf[f % (KD + 1)], min(KD, 15 - f));
+  static_for<KD>(kread);
+  static_for<16>([&](auto fc) {
+    constexpr int f = decltype(fc)::value;
+    if constexpr (f + KD < 16) kread(std::integral_constant<int, f + KD>{});
+    lgkm_wait<(15 - f < KD ? 15 - f : KD)>(kf[f % (KD + 1)]);
     sacc[f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[f % (KD + 1)], qf[f >> 1], sacc[f & 1], 0, 0, 0);
-  }
+  });
 }
 
-// O^T += V^T P^T over the V tile at LDS byte offset vb: 16 steps, ks = step/4
-// picks 16 keys, db = step%4 picks 32 dims.
-__device__ __forceinline__ void pv_tile(uint32_t vb, const uint32_t (&vaddr)[4], const bf16x8 (&pf)[4],
-                                        f32x16 (&oacc)[4]) {
+// O^T += V^T P^T over the V tile at LDS byte offset VOFF: 16 steps, ks =
+// step/4 picks 16 keys (4096 bytes further each), db = step%4 picks 32 dims
+// (vaddr[db]: absolute LDS address in a tile at offset 0).
+template <int VOFF>
+__device__ __forceinline__ void pv_tile(const uint32_t (&vaddr)[4], const bf16x8 (&pf)[4], f32x16 (&oacc)[4]) {
   s16x4 lo[KD + 1], hi[KD + 1];
-  auto vread = [&](int step) {
-    vt_read(vb + vaddr[step & 3] + (step >> 2) * 16 * 256, lo[step % (KD + 1)], hi[step % (KD + 1)]);
+  auto vread = [&](auto sc) {
+    constexpr int step = decltype(sc)::value;
+    vt_read<VOFF + (step >> 2) * 16 * 256>(vaddr[step & 3], lo[step % (KD + 1)], hi[step % (KD + 1)]);
   };
-#pragma unroll
-  for (int step = 0; step < KD; ++step) vread(step);
-#pragma unroll
-  for (int step = 0; step < 16; ++step) {
-    if (step + KD < 16) vread(step + KD);
-    const bf16x8 vf = vt_take(lo[step % (KD + 1)], hi[step % (KD + 1)], 2 * min(KD, 15 - step));
+  static_for<KD>(vread);
+  static_for<16>([&](auto sc) {
+    constexpr int step = decltype(sc)::value;
+    if constexpr (step + KD < 16) vread(std::integral_constant<int, step + KD>{});
+    const bf16x8 vf = vt_wait<2 * (15 - step < KD ? 15 - step : KD)>(lo[step % (KD + 1)], hi[step % (KD + 1)]);
     oacc[step & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[step >> 2], oacc[step & 3], 0, 0, 0);
-  }
+  });
 }
 
 // Eq. 4 mask of key tile kt for this lane's query row j (prefix keys up to
@@ -206,14 +194,15 @@ __device__ __forceinline__ void mask_tile(f32x16 (&sacc)[2], int kt, int g, int 
 // it does, and leaves P^T (bf16) in pf. Max and sums use independent chains.
 __device__ __forceinline__ void softmax_tile(const f32x16 (&sacc)[2], float c, float &ms, float (&ls)[2],
                                              f32x16 (&oacc)[4], bf16x8 (&pf)[4]) {
-  float m4[4];
+  float m2[2];  // one chain of three-input maxima per key block
 #pragma unroll
-  for (int t = 0; t < 4; ++t) m4[t] = fmaxf(sacc[t >> 1][8 * (t & 1)], sacc[t >> 1][8 * (t & 1) + 1]);
+  for (int b = 0; b < 2; ++b) {
+    m2[b] = fmaxf(fmaxf(sacc[b][0], sacc[b][1]), sacc[b][2]);
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int a = 2; a < 8; ++a) m4[t] = fmaxf(m4[t], sacc[t >> 1][8 * (t & 1) + a]);
-  float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    for (int a = 3; a < 15; a += 2) m2[b] = fmaxf(fmaxf(m2[b], sacc[b][a]), sacc[b][a + 1]);
+    m2[b] = fmaxf(m2[b], sacc[b][15]);
+  }
+  float mx = fmaxf(m2[0], m2[1]);
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float mcand = mx * c;
   const bool upd = mcand > ms + kRescaleThreshold;
@@ -331,7 +320,8 @@ __global__ __launch_bounds__(64 * TB * HP, 2) void attn_dma_kernel(
   // K: lane reads key 32*b + ql, chunk 2*kk + g -> slot (2*kk + g) ^ (ql & 15).
   uint32_t kaddr[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kaddr[kk] = uint32_t(ql) * 256u + 16u * uint32_t((2 * kk + g) ^ (ql & 15));
+  for (int kk = 0; kk < 8; ++kk)
+    kaddr[kk] = lds_addr(smem) + uint32_t(ql) * 256u + 16u * uint32_t((2 * kk + g) ^ (ql & 15));
   // V: 16-lane group G, e = (lane >> 2) & 3, qd = lane & 3: key 4*(G >> 1) + e (+16*ks, +8),
   // dims 32*db + 16*(G & 1) + 4*qd -> chunk 4*db + 2*(G & 1) + (qd >> 1), half (qd & 1).
   uint32_t vaddr[4];
@@ -341,7 +331,8 @@ __global__ __launch_bounds__(64 * TB * HP, 2) void attn_dma_kernel(
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int chunk = 4 * db + 2 * (G & 1) + (qd >> 1);
-      vaddr[db] = uint32_t(key) * 256u + 16u * uint32_t(chunk ^ (4 * (key & 3))) + 8u * uint32_t(qd & 1);
+      vaddr[db] = lds_addr(smem) + uint32_t(key) * 256u + 16u * uint32_t(chunk ^ (4 * (key & 3))) +
+                  8u * uint32_t(qd & 1);
     }
   }
 
@@ -374,20 +365,27 @@ __global__ __launch_bounds__(64 * TB * HP, 2) void attn_dma_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int it = 0; it < n_visit; ++it) {
+  // Visit `it` uses stage S = it % 2 (a template argument, so every LDS
+  // address is a fixed per-lane register plus an immediate offset).
+  constexpr int STAGE_BYTES = 2 * TILE * 2;  // K + V
+  auto visit = [&](int it, auto sc) {
+    constexpr int S = decltype(sc)::value;
     const int kt = tile_of(it);
-    const int stage = it & 1;
-    if (it + 1 < n_visit) issue_tile(tile_of(it + 1), stage ^ 1);
+    if (it + 1 < n_visit) issue_tile(tile_of(it + 1), S ^ 1);
     f32x16 sacc[2];
-    qk_tile(lds_addr(smem[stage][0]), kaddr, qf, sacc);
+    qk_tile<S * STAGE_BYTES>(kaddr, qf, sacc);
     const int ci = cls_base + kt;
     const int cls = (cls_words[ci >> 2] >> (8 * (ci & 3))) & 0xff;
     if ((cls != 2) || (kt * BN + BN > Tr)) mask_tile(sacc, kt, g, j, lq, jb);
     bf16x8 pf[4];
     softmax_tile(sacc, c, ms, ls, oacc, pf);
-    pv_tile(lds_addr(smem[stage][1]), vaddr, pf, oacc);
+    pv_tile<S * STAGE_BYTES + TILE * 2>(vaddr, pf, oacc);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA for the next tile has landed
     __syncthreads();                // ... and every wave's, and nobody reads this stage any more
+  };
+  for (int it = 0; it < n_visit; it += 2) {
+    visit(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_visit) visit(it + 1, std::integral_constant<int, 1>{});
   }
 
   if (row_ok) {
