@@ -13,7 +13,9 @@ from .mis import (  # noqa: F401
     logits,
     mask_rows,
     mis_mask,
+    rope,
     sis_attention,
+    sis_rope_attention,
     sis_scores,
     tile_classes,
     visible_pairs,

@@ -31,6 +31,11 @@ What it computes, from the pages' own statement of the method:
   causal mask; MIS must give the same item rows and scores (paper §4.1: the
   mask and reused positions give the item's last token the context it has
   in [q; c_i]; Table 1's release check).
+* Rotary embedding (the step before attention). The pages fix the positions
+  only (§4.1's position-id rule). The rotation is the usual rotary position
+  embedding of the decoder families the pages use: dims i and i + D/2 form a
+  pair turned by the angle pos * theta^(-2i/D). With it, MIS at the reused
+  positions must equal SIS at ordinary positions 0 .. Lq + S_i - 1.
 
 Readings where the pages are silent: softmax scale 1/sqrt(D) unless given;
 contiguous GQA groups; tile classes count in-range cells only (0 = no
@@ -261,6 +266,55 @@ def sis_attention(q, k, v, cu_seqlens, prefix_lens, cu_items, item_starts, *, sc
             s1 = base + (int(item_starts[i + 1]) if i + 1 < int(cu_items[r + 1]) else end - base)
             idx = np.concatenate([pre, np.arange(s0, s1)])
             o = causal_attention(qf[idx], kf[idx], vf[idx], scale=scale)
+            out[s0:s1] = o[lq:]
+    return out
+
+
+# --------------------------------------------------------------------------
+# rotary position embedding at the reused position ids
+# --------------------------------------------------------------------------
+
+
+def rope(x, pos, theta: float) -> np.ndarray:
+    """Rotary embedding of ``x`` ``[T, H, D]`` at positions ``pos`` ``[T]``, fp64.
+
+    Dims i and i + D/2 (i < D/2) are rotated by pos * theta^(-2i/D):
+    (a, b) -> (a cos - b sin, b cos + a sin).
+    """
+    xf = as_f64(x)
+    d = xf.shape[-1]
+    half = d // 2
+    inv = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    a, b = xf[..., :half], xf[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def sis_rope_attention(q, k, v, cu_seqlens, prefix_lens, cu_items, item_starts, theta: float, *,
+                       scale=None):
+    """Single-item scoring with rotary embedding: every [q; c_i] alone, rotated
+    at its own ordinary positions 0 .. Lq + S_i - 1, under a causal mask.
+
+    ``q``/``k`` are the un-rotated inputs. Returns ``[T, Hq, D]`` (prefix rows
+    from the prefix alone at positions 0 .. Lq - 1).
+    """
+    qf, kf, vf = as_f64(q), as_f64(k), as_f64(v)
+    out = np.zeros((qf.shape[0],) + qf.shape[1:])
+    for r in range(len(prefix_lens)):
+        base, end = int(cu_seqlens[r]), int(cu_seqlens[r + 1])
+        lq = int(prefix_lens[r])
+        pre = np.arange(base, base + lq)
+        if lq:
+            p = np.arange(lq)
+            out[pre] = causal_attention(rope(qf[pre], p, theta), rope(kf[pre], p, theta), vf[pre], scale=scale)
+        for i in range(int(cu_items[r]), int(cu_items[r + 1])):
+            s0 = base + int(item_starts[i])
+            s1 = base + (int(item_starts[i + 1]) if i + 1 < int(cu_items[r + 1]) else end - base)
+            idx = np.concatenate([pre, np.arange(s0, s1)])
+            p = np.arange(len(idx))
+            o = causal_attention(rope(qf[idx], p, theta), rope(kf[idx], p, theta), vf[idx], scale=scale)
             out[s0:s1] = o[lq:]
     return out
 
