@@ -241,6 +241,10 @@ def main(argv=None):
     t_sco = (back_to_back(lambda: mis.mis_score_labels(seg, hidd, Wd, labels, scores=scores, ws=ws,
                                                        stream=stream), n_rep)
              if has_score else 0.0)
+    # Rotary embedding at the reused positions (in place on q and k; run
+    # after the other kernels' timing since it changes q and k).
+    t_rope = back_to_back(lambda: mis.mis_apply_rope(seg, qd, kd, 1e6, stream=stream), n_rep)
+    rope_bytes = 2 * wl.total_tokens * (wl.hq + wl.hkv) * wl.d * 2  # read and write q, k (bf16)
     flops = attention_flops(wl)
     tflops = flops / (t_att * 1e-3) / 1e12
 
@@ -277,7 +281,7 @@ def main(argv=None):
         },
         "step_ms": {"segments": round(t_seg, 4), "attention": round(t_att_step, 4),
                     "score": round(t_sco_step, 4)},
-        "kernel_ms": {"attention": round(t_att, 4), "score": round(t_sco, 4)},
+        "kernel_ms": {"attention": round(t_att, 4), "score": round(t_sco, 4), "rope": round(t_rope, 4)},
         "roofline": {
             "kernel": "attn_dma_kernel (MIS prefill attention)",
             "bound": "mfma",
@@ -301,6 +305,14 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": b_lm,
             "algorithmic_flops_per_launch": f_lm,
         }
+    out["roofline_rope"] = {
+        "kernel": "rope_kernel (rotary embedding of q and k at the reused positions, not in the step)",
+        "bound": "hbm",
+        "achieved_gbs": round(rope_bytes / (t_rope * 1e-3) / 1e9, 1),
+        "peak_gbs": PEAK_HBM_GBS,
+        "frac": round(rope_bytes / (t_rope * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "algorithmic_bytes_per_launch": rope_bytes,
+    }
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
         b = torch.empty_like(a)

@@ -14,9 +14,10 @@
  * input order, columns in the requested label order (Scaling JEV-like
  * Decision Models with SGLang, "Getting Started with the Score API").
  *
- * Three stream-ordered calls:
+ * Stream-ordered calls:
  *   mis_build_segments    host metadata -> per-token item/position ids,
  *                         per-item readout positions, per-tile classes
+ *   mis_apply_rope        rotary embedding of Q and K at the reused positions
  *   mis_attention_prefill MIS prefill attention (skips fully masked tiles)
  *   mis_score_labels      readout gather -> LM head -> full-vocab logsumexp
  *                         -> label log-probs
@@ -156,6 +157,24 @@ int mis_attention_tile_shape(mis_dtype dt, int32_t hq, int32_t hkv, int32_t head
 int mis_attention_prefill(const mis_segments *seg, const void *q, const void *k, const void *v,
                           void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
                           float softmax_scale, void *stream);
+
+/*
+ * Rotary position embedding of Q and K in place, at the segment's position
+ * ids (paper §4.1's position-id rule: prefix token u at u, the token at
+ * offset d inside any item at Lq + d), so each item is rotated as if it
+ * followed the prefix alone and MIS equals single-item scoring with the
+ * rotation applied. Dims i and i + D/2 (i < D/2) of every head row are turned
+ * by pos * theta^(-2i/D): (a, b) -> (a cos - b sin, b cos + a sin); angles in
+ * fp64 reduced modulo 2 pi, products in fp32, bf16 results rounded to
+ * nearest even.
+ *
+ * q [T, hq, D] and k [T, hkv, D]: device, token-major, contiguous, element
+ * type dt, rewritten in place (call once per batch, before
+ * mis_attention_prefill). D must be 64 or 128; theta > 0 (for example 10000
+ * or 1000000). Errors: ARG, UNSUPPORTED, HIP.
+ */
+int mis_apply_rope(const mis_segments *seg, void *q, void *k, mis_dtype dt, int32_t hq, int32_t hkv,
+                   int32_t head_dim, float theta, void *stream);
 
 /*
  * Device workspace bytes of mis_score_labels for N items, vocabulary V,

@@ -1,10 +1,11 @@
 """Multiple-item scoring (MIS) hot path for AMD Instinct MI355X (gfx950).
 
 The computation lives in ``libmis.so`` (HIP kernels behind the C ABI of
-``include/mis.h``); this package is its ctypes binding. The three calls:
+``include/mis.h``); this package is its ctypes binding. The calls:
 
 * ``mis_build_segments``: per-token item/position ids, readout positions and
   per-tile classes from prefix lengths and item offsets;
+* ``mis_apply_rope``: rotary embedding of Q and K at the reused positions;
 * ``mis_attention_prefill``: MIS prefill attention on bf16 MFMA (or fp32);
 * ``mis_score_labels``: readout gather, LM-head contraction and full-vocab
   logsumexp, writing one label-score row per item.
@@ -28,6 +29,7 @@ from ._lib import (  # noqa: F401
     Segments,
     last_error,
     load,
+    mis_apply_rope,
     mis_attention_prefill,
     mis_attention_tile_shape,
     mis_build_segments,

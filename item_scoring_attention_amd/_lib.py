@@ -80,6 +80,9 @@ SIGNATURES = {
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]),
+    "mis_apply_rope": (ctypes.c_int, [ctypes.POINTER(MisSegments), ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_float, ctypes.c_void_p]),
     "mis_score_workspace_bytes": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32, ctypes.c_int,
                                                  ctypes.POINTER(ctypes.c_size_t)]),
@@ -287,6 +290,22 @@ def mis_attention_prefill(seg: Segments, q, k, v, o=None, softmax_scale: float =
                                         _dev(v, "v"), _dev(o, "o"), _dtype_code(q), q.shape[1],
                                         k.shape[1], q.shape[2], float(softmax_scale), _stream(stream)))
     return o
+
+
+def mis_apply_rope(seg: Segments, q, k, theta: float, stream=None):
+    """Rotary embedding of q ``[T,Hq,D]`` and k ``[T,Hkv,D]`` in place at the
+    segment position ids; returns (q, k)."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q and k must be [T, heads, D]")
+    if q.dtype != k.dtype:
+        raise ValueError("q and k must have the same dtype")
+    if q.shape[0] != seg.total_tokens or k.shape[0] != seg.total_tokens:
+        raise ValueError("token count of q/k differs from the segments")
+    if q.shape[2] != k.shape[2]:
+        raise ValueError("head_dim of q and k differ")
+    _check(load().mis_apply_rope(ctypes.byref(seg.struct), _dev(q, "q"), _dev(k, "k"), _dtype_code(q),
+                                 q.shape[1], k.shape[1], q.shape[2], float(theta), _stream(stream)))
+    return q, k
 
 
 # ---------------------------------------------------------------- scoring

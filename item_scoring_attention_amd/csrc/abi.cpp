@@ -357,6 +357,24 @@ int mis_attention_prefill(const mis_segments *seg, const void *q, const void *k,
   return ok();
 }
 
+int mis_apply_rope(const mis_segments *seg, void *q, void *k, mis_dtype dt, int32_t hq, int32_t hkv,
+                   int32_t head_dim, float theta, void *stream) {
+  if (!seg) return fail(MIS_ERR_ARG, "seg is NULL");
+  if (!q || !k) return fail(MIS_ERR_ARG, "q and k must be non-NULL");
+  if (hq < 1 || hkv < 1 || hq % hkv)
+    return fail(MIS_ERR_ARG, "need hq >= 1, hkv >= 1 and hq %% hkv == 0 (got %d, %d)", hq, hkv);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(MIS_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (dt != MIS_F32 && dt != MIS_BF16) return fail(MIS_ERR_UNSUPPORTED, "unknown dtype %d", int(dt));
+  if (!(theta > 0.f) || !std::isfinite(theta)) return fail(MIS_ERR_ARG, "theta must be a positive finite number");
+  if (seg->total_tokens < 1 || !seg->pos_id) return fail(MIS_ERR_ARG, "seg is not a built segment descriptor");
+  mis::RopeFreq f{};
+  for (int i = 0; i < head_dim / 2; ++i) f.inv[i] = std::pow(double(theta), -2.0 * i / head_dim);
+  hipError_t e = mis::launch_rope(*seg, q, k, dt, hq, hkv, head_dim, f, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope launch");
+  return ok();
+}
+
 int mis_score_workspace_bytes(int32_t num_items, int32_t vocab, int32_t num_labels, int32_t hidden,
                               mis_dtype dt, size_t *bytes) {
   if (!bytes) return fail(MIS_ERR_ARG, "bytes is NULL");

@@ -37,8 +37,16 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
                                  const void *v, void *o, int hq, int hkv, int d, float scale,
                                  hipStream_t stream);
 
-// Scoring workspace layout: partial maxima [N][nvt], partial sum-exp
-// [N][nvt], label logits [N][K] (all float32).
+// Inverse frequencies theta^(-2i/D) of the rotary embedding, i < D/2.
+struct RopeFreq {
+  double inv[64];
+};
+
+hipError_t launch_rope(const mis_segments &seg, void *q, void *k, mis_dtype dt, int hq, int hkv, int d,
+                       const RopeFreq &freq, hipStream_t stream);
+
+// Scoring workspace layout: partial maxima [nvt][N], partial sum-exp
+// [nvt][N], label logits [N][K] (all float32).
 inline int score_vocab_tiles(int vocab) { return (vocab + kScoreBlockV - 1) / kScoreBlockV; }
 
 hipError_t launch_score(const mis_segments &seg, const void *hidden, int h, const void *lm_head,

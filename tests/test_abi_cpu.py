@@ -185,3 +185,21 @@ def _gpu_visible():
 def test_valid_call_without_a_device_reports_hip_error():
     rc, msg = _build([0, 20], [4], [0, 2], [4, 10])
     assert rc == mis.MIS_ERR_HIP and msg
+
+
+def test_rope_argument_errors():
+    # every call below fails its host checks before anything is enqueued (the
+    # fake descriptor has no position ids), so no kernel ever sees its pointers
+    lib = mis.load()
+    s = _fake_seg()
+    p = ctypes.c_void_p(0x1000)
+    call = lambda seg, q, dt, hq, hkv, d, theta=1e4: lib.mis_apply_rope(seg, q, p, dt, hq, hkv, d, theta, None)
+    assert call(None, p, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_ARG
+    assert call(ctypes.byref(s), None, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_ARG
+    assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 3, 128) == mis.MIS_ERR_ARG
+    assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 4, 80) == mis.MIS_ERR_UNSUPPORTED
+    assert call(ctypes.byref(s), p, 7, 8, 4, 128) == mis.MIS_ERR_UNSUPPORTED
+    for theta in (0.0, -5.0, float("nan"), float("inf")):
+        assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 4, 128, theta) == mis.MIS_ERR_ARG
+    assert call(ctypes.byref(s), p, mis.MIS_F32, 8, 4, 64) == mis.MIS_ERR_ARG  # no position ids
+    assert "not a built segment" in mis.last_error()
