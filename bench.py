@@ -126,6 +126,92 @@ def cpu_baseline(wl, q, k, v, hid, W, labels, budget_s: float, flops: float):
     }
 
 
+def sweep(args) -> int:
+    """Request-size sweep: one packed MIS request against single-item scoring.
+
+    For each N, the items are scored (a) packed behind one shared prefix in a
+    single request (MIS) and (b) as N separate requests [q; c_i], each with
+    its own copy of the prefix, in one batched call (SIS). Both run the full
+    step (segments, attention, label scores) on the same model shape as the
+    single-request workload; the prefix is 744 tokens (the mean prompt length
+    the paper reports for its profile set) and each item 24 tokens plus its
+    delimiter (the compact prompt).
+    """
+    import torch
+
+    import item_scoring_attention_amd as mis
+    import workloads
+
+    torch.cuda.set_device(0)
+    base = workloads.config(2)
+    lq, item_len = 744, 25
+    stream = torch.cuda.current_stream()
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    def run(wl, steps):
+        q, k, v = workloads.qkv(wl)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        bm, bn = mis.mis_attention_tile_shape(mis.MIS_BF16, wl.hq, wl.hkv, wl.d)
+        seg_buf = torch.empty(mis.mis_segments_bytes(wl.cu_seqlens, wl.total_items, bm, bn),
+                              dtype=torch.uint8, device="cuda")
+        seg = mis.mis_build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, bm, bn,
+                                     dev_buf=seg_buf)
+        hid = np.zeros((wl.total_tokens, wl.hidden), dtype=np.uint16)
+        hid[seg.array("readout_pos").cpu().numpy()] = workloads.readout_values(wl)
+        hidd, Wd = dev(hid), dev(workloads.lm_head(wl))
+        labels = workloads.label_ids(wl)
+        scores = torch.empty((wl.total_items, wl.num_labels), dtype=torch.float32, device="cuda")
+        ws = torch.empty(mis.mis_score_workspace_bytes(wl.total_items, wl.vocab, wl.num_labels, wl.hidden,
+                                                       mis.MIS_BF16), dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(qd)
+
+        def step():
+            sg = mis.mis_build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, bm, bn,
+                                        dev_buf=seg_buf, stream=stream)
+            mis.mis_attention_prefill(sg, qd, kd, vd, o=o, stream=stream)
+            mis.mis_score_labels(sg, hidd, Wd, labels, scores=scores, ws=ws, stream=stream)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    rows = []
+    for n in (1, 5, 20, 50, 100, 200):
+        kw = dict(hq=base.hq, hkv=base.hkv, d=base.d, hidden=base.hidden, vocab=base.vocab,
+                  num_labels=base.num_labels, seed=7)
+        wl_mis = workloads.from_lengths(f"sweep-mis-{n}", [lq], [[item_len] * n], **kw)
+        wl_sis = workloads.from_lengths(f"sweep-sis-{n}", [lq] * n, [[item_len]] * n, **kw)
+        t_mis, t_sis = run(wl_mis, args.steps), run(wl_sis, args.steps)
+        rows.append({
+            "items": n,
+            "mis_ms_per_step": round(t_mis * 1e3, 4),
+            "sis_ms_per_step": round(t_sis * 1e3, 4),
+            "mis_item_scores_per_s": round(n / t_mis, 1),
+            "sis_item_scores_per_s": round(n / t_sis, 1),
+            "speedup": round(t_sis / t_mis, 3),
+            "mis_prefill_tokens_per_item": round((lq + n * item_len) / n, 1),
+            "sis_prefill_tokens_per_item": lq + item_len,
+            "mis_attention_gflop": round(attention_flops(wl_mis) / 1e9, 3),
+            "sis_attention_gflop": round(attention_flops(wl_sis) / 1e9, 3),
+        })
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "MIS vs single-item scoring, whole step, 1 GPU", "unit": "item scores/s",
+        "steps": args.steps, "data": "synthetic",
+        "config": {"workload": "request-size sweep", "prefix": lq, "item_tokens": item_len,
+                   "hq": base.hq, "hkv": base.hkv, "head_dim": base.d, "hidden": base.hidden,
+                   "vocab": base.vocab, "labels": base.num_labels},
+        "sweep": rows}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +220,8 @@ def main(argv=None):
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--sweep", action="store_true",
+                    help="request-size sweep (N = 1 .. 200 items): packed MIS against single-item scoring")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args(argv)
@@ -151,6 +239,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.sweep:
+        return sweep(args)
     torch.cuda.set_device(0)
     wl = workloads.config(args.config)
     if wl.dtype != "bf16":
