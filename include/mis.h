@@ -19,8 +19,10 @@
  *                         per-item readout positions, per-tile classes
  *   mis_apply_rope        rotary embedding of Q and K at the reused positions
  *   mis_attention_prefill MIS prefill attention (skips fully masked tiles)
+ *   mis_attention_append  the same for item rows only, against a cached prefix
  *   mis_score_labels      readout gather -> LM head -> full-vocab logsumexp
- *                         -> label log-probs
+ *                         -> label log-probs (mis_score_labels_at: at any
+ *                         token rows, e.g. several markers per item)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -159,6 +161,22 @@ int mis_attention_prefill(const mis_segments *seg, const void *q, const void *k,
                           float softmax_scale, void *stream);
 
 /*
+ * Item rows only, against a cached prefix: the same attention as
+ * mis_attention_prefill for every item row (the prefix K/V rows are read as
+ * they are in k and v, e.g. kept from an earlier pass over the same prefix),
+ * without recomputing the prefix rows (From Generation to Scoring, §4.4: a
+ * request that carries part of the items prefills the query again unless
+ * its prefix is reused). Arguments, layout and errors as for
+ * mis_attention_prefill. On return every item row of o holds its result; a
+ * prefix row of o either keeps its old contents or, when its 64-row query tile
+ * also holds item rows, is rewritten with the value mis_attention_prefill
+ * writes.
+ */
+int mis_attention_append(const mis_segments *seg, const void *q, const void *k, const void *v,
+                         void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                         float softmax_scale, void *stream);
+
+/*
  * Rotary position embedding of Q and K in place, at the segment's position
  * ids (paper §4.1's position-id rule: prefix token u at u, the token at
  * offset d inside any item at Lq + d), so each item is rotated as if it
@@ -203,6 +221,27 @@ int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden
                      const void *lm_head, int32_t vocab, mis_dtype dt, const int32_t *label_ids_h,
                      int32_t num_labels, int32_t apply_softmax, float *scores, void *ws,
                      size_t ws_bytes, void *stream);
+
+/*
+ * Label scores at caller-chosen token rows: one row of K label scores for
+ * each entry of positions_h, from hidden[positions_h[r]], computed exactly as
+ * in mis_score_labels. This serves several readout markers per item (setwise
+ * scoring, JEV post's score extraction positions) and graded multi-class
+ * labels (paper §9: several single-token class labels normalised together,
+ * with apply_softmax).
+ *
+ * positions_h: host [num_rows], each in [0, num_tokens), read before return.
+ * hidden [num_tokens, H], lm_head [V, H]: device, element type dt. scores:
+ * device float32 [num_rows, K] (may be NULL when num_rows = 0). ws/ws_bytes:
+ * device workspace of at least mis_score_workspace_bytes(num_rows, ...); the
+ * positions are staged into it through the pinned host ring.
+ * Errors: ARG (incl. a position out of range), LABEL, WORKSPACE,
+ * UNSUPPORTED, HIP.
+ */
+int mis_score_labels_at(const int32_t *positions_h, int32_t num_rows, int32_t num_tokens,
+                        const void *hidden, int32_t hidden_size, const void *lm_head, int32_t vocab,
+                        mis_dtype dt, const int32_t *label_ids_h, int32_t num_labels,
+                        int32_t apply_softmax, float *scores, void *ws, size_t ws_bytes, void *stream);
 
 /* Text of the last error on this thread ("" if none). Never NULL. */
 const char *mis_last_error(void);

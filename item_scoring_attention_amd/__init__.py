@@ -7,8 +7,10 @@ The computation lives in ``libmis.so`` (HIP kernels behind the C ABI of
   per-tile classes from prefix lengths and item offsets;
 * ``mis_apply_rope``: rotary embedding of Q and K at the reused positions;
 * ``mis_attention_prefill``: MIS prefill attention on bf16 MFMA (or fp32);
+  ``mis_attention_append``: the same for item rows only, against a cached prefix;
 * ``mis_score_labels``: readout gather, LM-head contraction and full-vocab
-  logsumexp, writing one label-score row per item.
+  logsumexp, writing one label-score row per item (``mis_score_labels_at``:
+  at any token rows, e.g. several readout markers per item).
 """
 from ._lib import (  # noqa: F401
     LIB_PATH,
@@ -30,10 +32,12 @@ from ._lib import (  # noqa: F401
     last_error,
     load,
     mis_apply_rope,
+    mis_attention_append,
     mis_attention_prefill,
     mis_attention_tile_shape,
     mis_build_segments,
     mis_score_labels,
+    mis_score_labels_at,
     mis_score_workspace_bytes,
     mis_segments_bytes,
     version,

@@ -80,6 +80,10 @@ SIGNATURES = {
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]),
+    "mis_attention_append": (ctypes.c_int, [ctypes.POINTER(MisSegments), ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]),
     "mis_apply_rope": (ctypes.c_int, [ctypes.POINTER(MisSegments), ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_float, ctypes.c_void_p]),
@@ -90,6 +94,10 @@ SIGNATURES = {
                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_int, _i32p,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mis_score_labels_at": (ctypes.c_int, [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int,
+                                           _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mis_last_error": (ctypes.c_char_p, []),
     "mis_version": (ctypes.c_char_p, []),
 }
@@ -273,6 +281,15 @@ def mis_attention_tile_shape(dtype, hq: int, hkv: int, head_dim: int):
 
 def mis_attention_prefill(seg: Segments, q, k, v, o=None, softmax_scale: float = 0.0, stream=None):
     """MIS attention. q ``[T,Hq,D]``, k/v ``[T,Hkv,D]``; returns o ``[T,Hq,D]``."""
+    return _attention("mis_attention_prefill", seg, q, k, v, o, softmax_scale, stream)
+
+
+def mis_attention_append(seg: Segments, q, k, v, o, softmax_scale: float = 0.0, stream=None):
+    """Item rows only against a cached prefix (prefix rows of ``o`` are not recomputed)."""
+    return _attention("mis_attention_append", seg, q, k, v, o, softmax_scale, stream)
+
+
+def _attention(fn: str, seg: Segments, q, k, v, o, softmax_scale: float, stream):
     torch = _torch()
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be [T, heads, D]")
@@ -286,9 +303,9 @@ def mis_attention_prefill(seg: Segments, q, k, v, o=None, softmax_scale: float =
         o = torch.empty_like(q)
     elif o.shape != q.shape or o.dtype != q.dtype:
         raise ValueError("o must match q in shape and dtype")
-    _check(load().mis_attention_prefill(ctypes.byref(seg.struct), _dev(q, "q"), _dev(k, "k"),
-                                        _dev(v, "v"), _dev(o, "o"), _dtype_code(q), q.shape[1],
-                                        k.shape[1], q.shape[2], float(softmax_scale), _stream(stream)))
+    _check(getattr(load(), fn)(ctypes.byref(seg.struct), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                               _dev(o, "o"), _dtype_code(q), q.shape[1], k.shape[1], q.shape[2],
+                               float(softmax_scale), _stream(stream)))
     return o
 
 
@@ -346,4 +363,30 @@ def mis_score_labels(seg: Segments, hidden, lm_head, label_ids: Sequence[int],
                                    _ptr_i32(lab), K, 1 if apply_softmax else 0,
                                    _dev(scores, "scores"), _dev(ws, "ws"),
                                    ws.numel() * ws.element_size(), _stream(stream)))
+    return scores
+
+
+def mis_score_labels_at(positions, hidden, lm_head, label_ids: Sequence[int], apply_softmax: bool = False,
+                        scores=None, ws=None, stream=None):
+    """Label scores ``[R, K]`` (float32) at the token rows ``positions`` (host ints)."""
+    torch = _torch()
+    if hidden.dim() != 2 or lm_head.dim() != 2 or hidden.shape[1] != lm_head.shape[1]:
+        raise ValueError("hidden must be [T, H] and lm_head [V, H]")
+    if hidden.dtype != lm_head.dtype:
+        raise ValueError("hidden and lm_head dtypes differ")
+    pos = _host_i32(positions)
+    lab = _host_i32(label_ids)
+    R, K = len(pos), len(lab)
+    H, V = hidden.shape[1], lm_head.shape[0]
+    if scores is None:
+        scores = torch.empty((R, K), dtype=torch.float32, device=hidden.device)
+    elif scores.dtype != torch.float32 or tuple(scores.shape) != (R, K):
+        raise ValueError("scores must be float32 [R, K]")
+    if ws is None:
+        nbytes = mis_score_workspace_bytes(R, V, max(K, 1), H, hidden.dtype) if K >= 1 else 256
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=hidden.device)
+    _check(load().mis_score_labels_at(_ptr_i32(pos), R, hidden.shape[0], _dev(hidden, "hidden"), H,
+                                      _dev(lm_head, "lm_head"), V, _dtype_code(hidden), _ptr_i32(lab), K,
+                                      1 if apply_softmax else 0, _dev(scores, "scores"), _dev(ws, "ws"),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
     return scores

@@ -37,6 +37,14 @@ int hip_fail(hipError_t e, const char *what) {
 
 constexpr size_t kAlign = 256;
 
+size_t align_up(size_t x);
+
+// Byte offset of the readout positions inside the scoring workspace (after
+// the partial maxima, partial sums and label logits of n rows).
+size_t score_ws_positions_offset(size_t n, size_t nvt, int32_t num_labels) {
+  return align_up(sizeof(float) * n * nvt) * 2 + align_up(sizeof(float) * n * size_t(num_labels));
+}
+
 // Pinned host staging for metadata uploads. A copy from pageable memory makes
 // the host wait for the stream, so the next launches could not be queued
 // ahead of the GPU. Each device gets a small ring of page-locked slots; a slot
@@ -331,9 +339,11 @@ int mis_attention_tile_shape(mis_dtype dt, int32_t hq, int32_t hkv, int32_t head
   return ok();
 }
 
-int mis_attention_prefill(const mis_segments *seg, const void *q, const void *k, const void *v,
-                          void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
-                          float softmax_scale, void *stream) {
+namespace {
+
+int attention_call(const mis_segments *seg, const void *q, const void *k, const void *v, void *o,
+                   mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim, float softmax_scale,
+                   int items_only, void *stream) {
   if (!seg) return fail(MIS_ERR_ARG, "seg is NULL");
   if (!q || !k || !v || !o) return fail(MIS_ERR_ARG, "q, k, v and o must be non-NULL");
   int32_t bm, bn;
@@ -348,13 +358,27 @@ int mis_attention_prefill(const mis_segments *seg, const void *q, const void *k,
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = dt == MIS_BF16
-                     ? mis::launch_attention_bf16(*seg, q, k, v, o, hq, hkv, head_dim, scale, st)
+                     ? mis::launch_attention_bf16(*seg, q, k, v, o, hq, hkv, head_dim, scale, items_only, st)
                      : mis::launch_attention_f32(*seg, static_cast<const float *>(q),
                                                  static_cast<const float *>(k),
                                                  static_cast<const float *>(v), static_cast<float *>(o),
-                                                 hq, hkv, head_dim, scale, st);
+                                                 hq, hkv, head_dim, scale, items_only, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
+}
+
+}  // namespace
+
+int mis_attention_prefill(const mis_segments *seg, const void *q, const void *k, const void *v,
+                          void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                          float softmax_scale, void *stream) {
+  return attention_call(seg, q, k, v, o, dt, hq, hkv, head_dim, softmax_scale, 0, stream);
+}
+
+int mis_attention_append(const mis_segments *seg, const void *q, const void *k, const void *v,
+                         void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                         float softmax_scale, void *stream) {
+  return attention_call(seg, q, k, v, o, dt, hq, hkv, head_dim, softmax_scale, 1, stream);
 }
 
 int mis_apply_rope(const mis_segments *seg, void *q, void *k, mis_dtype dt, int32_t hq, int32_t hkv,
@@ -385,7 +409,7 @@ int mis_score_workspace_bytes(int32_t num_items, int32_t vocab, int32_t num_labe
   if (dt != MIS_F32 && dt != MIS_BF16) return fail(MIS_ERR_UNSUPPORTED, "unknown dtype %d", int(dt));
   const size_t nvt = size_t(mis::score_vocab_tiles(vocab));
   const size_t n = size_t(std::max(num_items, 1));
-  *bytes = align_up(sizeof(float) * n * nvt) * 2 + align_up(sizeof(float) * n * num_labels);
+  *bytes = score_ws_positions_offset(n, nvt, num_labels) + align_up(sizeof(int32_t) * n);
   return ok();
 }
 
@@ -411,9 +435,44 @@ int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden
   mis::LabelArgs la{};
   la.k = num_labels;
   std::memcpy(la.ids, label_ids_h, sizeof(int32_t) * num_labels);
-  hipError_t e = mis::launch_score(*seg, hidden, hidden_size, lm_head, vocab, dt, la,
+  hipError_t e = mis::launch_score(seg->readout_pos, seg->total_items, hidden, hidden_size, lm_head, vocab, dt, la,
                                    apply_softmax ? 1 : 0, scores, static_cast<float *>(ws),
                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "scoring launch");
+  return ok();
+}
+
+int mis_score_labels_at(const int32_t *positions_h, int32_t num_rows, int32_t num_tokens,
+                        const void *hidden, int32_t hidden_size, const void *lm_head, int32_t vocab,
+                        mis_dtype dt, const int32_t *label_ids_h, int32_t num_labels,
+                        int32_t apply_softmax, float *scores, void *ws, size_t ws_bytes, void *stream) {
+  if (num_rows < 0 || num_tokens < 1) return fail(MIS_ERR_ARG, "need num_rows >= 0 and num_tokens >= 1");
+  if (num_rows > 0 && (!positions_h || !scores)) return fail(MIS_ERR_ARG, "positions and scores must be non-NULL");
+  if (!hidden || !lm_head || !ws) return fail(MIS_ERR_ARG, "hidden, lm_head and ws must be non-NULL");
+  if (!label_ids_h) return fail(MIS_ERR_ARG, "label_ids is NULL");
+  size_t need;
+  int rc = mis_score_workspace_bytes(num_rows, vocab, num_labels, hidden_size, dt, &need);
+  if (rc) return rc;
+  for (int32_t i = 0; i < num_labels; ++i)
+    if (label_ids_h[i] < 0 || label_ids_h[i] >= vocab)
+      return fail(MIS_ERR_LABEL, "label id %d at position %d outside [0, %d)", label_ids_h[i], i, vocab);
+  for (int32_t i = 0; i < num_rows; ++i)
+    if (positions_h[i] < 0 || positions_h[i] >= num_tokens)
+      return fail(MIS_ERR_ARG, "position %d at index %d outside [0, %d)", positions_h[i], i, num_tokens);
+  if (ws_bytes < need) return fail(MIS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, need);
+  if (dt == MIS_BF16 && hidden_size % 32)
+    return fail(MIS_ERR_UNSUPPORTED, "bf16 scoring needs hidden_size %% 32 == 0 (got %d)", hidden_size);
+  if (num_rows == 0) return ok();
+  const size_t off = score_ws_positions_offset(size_t(num_rows), size_t(mis::score_vocab_tiles(vocab)), num_labels);
+  int32_t *pos_dev = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(ws) + off);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = stage_ring().upload(pos_dev, positions_h, sizeof(int32_t) * size_t(num_rows), st);
+  if (e != hipSuccess) return hip_fail(e, "staging readout positions");
+  mis::LabelArgs la{};
+  la.k = num_labels;
+  std::memcpy(la.ids, label_ids_h, sizeof(int32_t) * num_labels);
+  e = mis::launch_score(pos_dev, num_rows, hidden, hidden_size, lm_head, vocab, dt, la, apply_softmax ? 1 : 0,
+                        scores, static_cast<float *>(ws), st);
   if (e != hipSuccess) return hip_fail(e, "scoring launch");
   return ok();
 }

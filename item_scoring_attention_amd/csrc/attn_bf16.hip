@@ -237,7 +237,7 @@ __global__ __launch_bounds__(64 * TB * HP, 2) void attn_dma_kernel(
     const int8_t *__restrict__ tile_class, const int32_t *__restrict__ item_id,
     const int32_t *__restrict__ item_begin, const __bf16 *__restrict__ q,
     const __bf16 *__restrict__ k, const __bf16 *__restrict__ v, __bf16 *__restrict__ o, int hq,
-    int hkv, float c /* softmax scale * log2(e) */) {
+    int hkv, float c /* softmax scale * log2(e) */, int items_only) {
   constexpr int NW = TB * HP;             // waves
   constexpr int BMT = 32 * TB;            // query tokens per workgroup
   constexpr int TILE = BN * D;            // bf16 elements of one K or V tile
@@ -260,6 +260,9 @@ __global__ __launch_bounds__(64 * TB * HP, 2) void attn_dma_kernel(
   const int base = cu_seqlens[r];
   const int Tr = cu_seqlens[r + 1] - base;
   const int lq = prefix_lens[r];
+  // Appending items to a cached prefix: a query tile that holds prefix rows
+  // only has nothing to compute (the whole workgroup leaves together).
+  if (items_only && qt * BMT + BMT <= lq) return;
   const int nkt = (Tr + BN - 1) / BN;
   const int j1 = min(Tr, qt * BMT + BMT);
   const int b_hi = (j1 + BN - 1) / BN;
@@ -419,12 +422,12 @@ int device_cus() {
 
 template <int TB, int HP>
 hipError_t launch_variant(const mis_segments &seg, const __bf16 *qp, const __bf16 *kp, const __bf16 *vp,
-                          __bf16 *op, int hq, int hkv, float c, hipStream_t st) {
+                          __bf16 *op, int hq, int hkv, float c, int items_only, hipStream_t st) {
   const int64_t blocks = int64_t(seg.num_work) * hq / HP;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   attn_dma_kernel<TB, HP><<<dim3(unsigned(blocks)), 64 * TB * HP, 0, st>>>(
       seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.item_id,
-      seg.item_begin, qp, kp, vp, op, hq, hkv, c);
+      seg.item_begin, qp, kp, vp, op, hq, hkv, c, items_only);
   return hipGetLastError();
 }
 
@@ -432,7 +435,7 @@ hipError_t launch_variant(const mis_segments &seg, const __bf16 *qp, const __bf1
 
 hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const void *k,
                                  const void *v, void *o, int hq, int hkv, int d, float scale,
-                                 hipStream_t st) {
+                                 int items_only, hipStream_t st) {
   if (d != D) return hipErrorInvalidValue;
   const int gsz = hq / hkv;
   const float c = scale * kLog2e;
@@ -444,10 +447,10 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
   // staging per FLOP but leave half as many workgroups to balance: taken only
   // when every CU still gets at least 8 of them.
   if (gsz % 4 == 0 && int64_t(seg.num_work) * (hq / 4) >= 8 * int64_t(device_cus()))
-    return launch_variant<2, 4>(seg, qp, kp, vp, op, hq, hkv, c, st);
+    return launch_variant<2, 4>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
   if (gsz % 2 == 0)  // 2 token blocks x 2 heads of one KV head
-    return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, st);
-  return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, st);  // odd group size
+    return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
+  return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);  // odd group size
 }
 
 }  // namespace mis

@@ -14,7 +14,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     int B, int T, int hq, int hkv, float scale, const int32_t *__restrict__ cu_seqlens,
     const int32_t *__restrict__ prefix_lens, const int32_t *__restrict__ item_id,
     const int32_t *__restrict__ item_begin, const float *__restrict__ q,
-    const float *__restrict__ k, const float *__restrict__ v, float *__restrict__ o) {
+    const float *__restrict__ k, const float *__restrict__ v, float *__restrict__ o, int items_only) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
   if (t >= T) return;
@@ -27,6 +27,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   const int32_t base = cu_seqlens[lo];
   const int32_t lq = prefix_lens[lo];
   const int32_t u = t - base;
+  if (items_only && u < lq) return;  // appending items to a cached prefix: prefix rows are not recomputed
   const int g = (h * hkv) / hq;
   const int64_t kv_stride = int64_t(hkv) * D;
 
@@ -71,16 +72,16 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 
 hipError_t launch_attention_f32(const mis_segments &seg, const float *q, const float *k,
                                 const float *v, float *o, int hq, int hkv, int d, float scale,
-                                hipStream_t st) {
+                                int items_only, hipStream_t st) {
   const dim3 grid((seg.total_tokens + 63) / 64, hq);
   if (d == 64) {
     attn_f32_kernel<64><<<grid, 64, 0, st>>>(seg.num_requests, seg.total_tokens, hq, hkv, scale,
                                              seg.cu_seqlens, seg.prefix_lens, seg.item_id,
-                                             seg.item_begin, q, k, v, o);
+                                             seg.item_begin, q, k, v, o, items_only);
   } else if (d == 128) {
     attn_f32_kernel<128><<<grid, 64, 0, st>>>(seg.num_requests, seg.total_tokens, hq, hkv, scale,
                                               seg.cu_seqlens, seg.prefix_lens, seg.item_id,
-                                              seg.item_begin, q, k, v, o);
+                                              seg.item_begin, q, k, v, o, items_only);
   } else {
     return hipErrorInvalidValue;
   }

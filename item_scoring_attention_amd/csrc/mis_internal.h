@@ -29,13 +29,15 @@ struct LabelArgs {
 hipError_t launch_segments(const mis_segments &seg, const int32_t *item_starts_dev,
                            hipStream_t stream);
 
+// items_only != 0: rows of query tiles that hold prefix rows only are not
+// computed (appending items to a cached prefix).
 hipError_t launch_attention_f32(const mis_segments &seg, const float *q, const float *k,
                                 const float *v, float *o, int hq, int hkv, int d, float scale,
-                                hipStream_t stream);
+                                int items_only, hipStream_t stream);
 
 hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const void *k,
                                  const void *v, void *o, int hq, int hkv, int d, float scale,
-                                 hipStream_t stream);
+                                 int items_only, hipStream_t stream);
 
 // Inverse frequencies theta^(-2i/D) of the rotary embedding, i < D/2.
 struct RopeFreq {
@@ -46,10 +48,12 @@ hipError_t launch_rope(const mis_segments &seg, void *q, void *k, mis_dtype dt, 
                        const RopeFreq &freq, hipStream_t stream);
 
 // Scoring workspace layout: partial maxima [nvt][N], partial sum-exp
-// [nvt][N], label logits [N][K] (all float32).
+// [nvt][N], label logits [N][K] (all float32), then N int32 readout
+// positions (used by mis_score_labels_at).
 inline int score_vocab_tiles(int vocab) { return (vocab + kScoreBlockV - 1) / kScoreBlockV; }
 
-hipError_t launch_score(const mis_segments &seg, const void *hidden, int h, const void *lm_head,
+// N rows of label scores from the hidden rows at readout_pos[0 .. N-1].
+hipError_t launch_score(const int32_t *readout_pos, int num_rows, const void *hidden, int h, const void *lm_head,
                         int vocab, mis_dtype dt, const LabelArgs &labels, int apply_softmax,
                         float *scores, float *ws, hipStream_t stream);
 

@@ -425,10 +425,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_score(const mis_segments &seg, const void *hidden, int H, const void *lm_head,
+hipError_t launch_score(const int32_t *readout_pos, int N, const void *hidden, int H, const void *lm_head,
                         int V, mis_dtype dt, const LabelArgs &labels, int apply_softmax,
                         float *scores, float *ws, hipStream_t st) {
-  const int N = seg.total_items;
   const int nvt = score_vocab_tiles(V);
   const size_t part = ((sizeof(float) * size_t(N) * nvt + 255) / 256) * 256;
   float *pmax = ws;
@@ -444,28 +443,28 @@ hipError_t launch_score(const mis_segments &seg, const void *hidden, int H, cons
       const int nit = (N + 32 * ni - 1) / (32 * ni);
       const unsigned grid = unsigned((nvt + 7) / 8 * 8 * nit);
       if (ni == 1)
-        score_lds_kernel<1, 3><<<grid, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum,
+        score_lds_kernel<1, 3><<<grid, 256, 0, st>>>(hp, wp, H, V, N, readout_pos, labels, pmax, psum,
                                                      plab, nvt, nit);
       else if (ni == 2)
-        score_lds_kernel<2, 3><<<grid, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum,
+        score_lds_kernel<2, 3><<<grid, 256, 0, st>>>(hp, wp, H, V, N, readout_pos, labels, pmax, psum,
                                                      plab, nvt, nit);
       else
-        score_lds_kernel<4, 2><<<grid, 256, 0, st>>>(hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum,
+        score_lds_kernel<4, 2><<<grid, 256, 0, st>>>(hp, wp, H, V, N, readout_pos, labels, pmax, psum,
                                                      plab, nvt, nit);
     } else if (N <= 64) {
       score_bf16_kernel<1><<<dim3(nvt, (N + 63) / 64), 256, 0, st>>>(
-          hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum, plab, nvt);
+          hp, wp, H, V, N, readout_pos, labels, pmax, psum, plab, nvt);
     } else if (N <= 128) {
       score_bf16_kernel<2><<<dim3(nvt, (N + 127) / 128), 256, 0, st>>>(
-          hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum, plab, nvt);
+          hp, wp, H, V, N, readout_pos, labels, pmax, psum, plab, nvt);
     } else {
       score_bf16_kernel<4><<<dim3(nvt, (N + 255) / 256), 256, 0, st>>>(
-          hp, wp, H, V, N, seg.readout_pos, labels, pmax, psum, plab, nvt);
+          hp, wp, H, V, N, readout_pos, labels, pmax, psum, plab, nvt);
     }
   } else {
     score_f32_kernel<<<dim3(nvt, N), BV, 0, st>>>(static_cast<const float *>(hidden),
                                                   static_cast<const float *>(lm_head), H, V, N,
-                                                  seg.readout_pos, labels, pmax, psum, plab, nvt);
+                                                  readout_pos, labels, pmax, psum, plab, nvt);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -138,6 +138,11 @@ def test_attention_argument_errors():
     assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 4, 128, float("nan")) == mis.MIS_ERR_ARG
     s2 = _fake_seg(bm=32)
     assert call(ctypes.byref(s2), p, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_UNSUPPORTED
+    # the item-rows-only entry point runs the same host checks
+    call = lambda seg, q, dt, hq, hkv, d, sc=0.0: lib.mis_attention_append(seg, q, p, p, p, dt, hq, hkv, d, sc, None)
+    assert call(None, p, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_ARG
+    assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 3, 128) == mis.MIS_ERR_ARG
+    assert call(ctypes.byref(s2), p, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_UNSUPPORTED
 
 
 def test_score_argument_errors():
@@ -203,3 +208,23 @@ def test_rope_argument_errors():
         assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 4, 128, theta) == mis.MIS_ERR_ARG
     assert call(ctypes.byref(s), p, mis.MIS_F32, 8, 4, 64) == mis.MIS_ERR_ARG  # no position ids
     assert "not a built segment" in mis.last_error()
+
+
+def test_score_at_argument_errors():
+    # positions and labels are checked on the host before anything is enqueued
+    lib = mis.load()
+    p = ctypes.c_void_p(0x1000)
+    lab = np.asarray([3, 7], dtype=np.int32)
+    def call(pos, nrows, ntok=100, labels=lab, k=2, ws_bytes=1 << 30, dt=mis.MIS_BF16, h=256):
+        pos = np.asarray(pos, dtype=np.int32)
+        labels = np.asarray(labels, dtype=np.int32)
+        return lib.mis_score_labels_at(pos.ctypes.data if pos.size else None, nrows, ntok, p, h, p, 1000, dt,
+                                       labels.ctypes.data, k, 0, p, p, ws_bytes, None)
+    assert call([5, 100], 2) == mis.MIS_ERR_ARG and "outside" in mis.last_error()
+    assert call([-1], 1) == mis.MIS_ERR_ARG
+    assert call([5], 1, labels=[3, 1000]) == mis.MIS_ERR_LABEL
+    assert call([5], 1, k=0) == mis.MIS_ERR_LABEL
+    assert call([5], 1, ws_bytes=16) == mis.MIS_ERR_WORKSPACE
+    assert call([5], 1, h=100) == mis.MIS_ERR_UNSUPPORTED
+    assert call([5], -1) == mis.MIS_ERR_ARG
+    assert call([], 0) == mis.MIS_OK  # nothing to score: validated, nothing enqueued
