@@ -21,7 +21,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmis.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "segments.hip", "rope.hip", "attn_f32.hip", "attn_bf16.hip", "score.hip"]
+SOURCES = ["abi.cpp", "segments.hip", "rope.hip", "attn_f32.hip", "attn_bf16.hip", "attn_bf16_pipe.hip",
+           "score.hip"]
 
 # Per-source extra flags. The attention kernels keep their MFMA accumulators
 # in VGPRs: with the default heuristic the allocator parks them in AGPRs and

@@ -438,19 +438,14 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
                                  int items_only, hipStream_t st) {
   if (d != D) return hipErrorInvalidValue;
   const int gsz = hq / hkv;
+  // Even group sizes (every GQA shape of the workloads) take the kernel with
+  // 64 query rows per wave; odd ones (MHA included) this one, one head per
+  // workgroup.
+  if (gsz % 2 == 0) return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, st);
   const float c = scale * kLog2e;
-  const __bf16 *qp = static_cast<const __bf16 *>(q);
-  const __bf16 *kp = static_cast<const __bf16 *>(k);
-  const __bf16 *vp = static_cast<const __bf16 *>(v);
-  __bf16 *op = static_cast<__bf16 *>(o);
-  // 4 heads per workgroup (8 waves, one workgroup per CU) halve the K/V
-  // staging per FLOP but leave half as many workgroups to balance: taken only
-  // when every CU still gets at least 8 of them.
-  if (gsz % 4 == 0 && int64_t(seg.num_work) * (hq / 4) >= 8 * int64_t(device_cus()))
-    return launch_variant<2, 4>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
-  if (gsz % 2 == 0)  // 2 token blocks x 2 heads of one KV head
-    return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
-  return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);  // odd group size
+  return launch_variant<2, 1>(seg, static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
+                              static_cast<const __bf16 *>(v), static_cast<__bf16 *>(o), hq, hkv, c, items_only,
+                              st);
 }
 
 }  // namespace mis

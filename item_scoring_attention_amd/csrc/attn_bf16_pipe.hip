@@ -1,0 +1,310 @@
+// bf16 MIS prefill attention on CDNA4 MFMA (gfx950), 64 query rows per wave.
+//
+// Computes O = softmax(scale * Q K^T + M) V per query head with the mask M of
+// From Generation to Scoring, §4.1, Eq. 4 (a prefix row sees the prefix up to
+// itself; an item row sees the whole prefix and its own item up to itself),
+// visiting only the key tiles a query tile can see (§4.3: the MIS kernels
+// skip fully masked tiles; the SGLang blog lists the same change for its
+// FlashInfer kernels).
+//
+// Why 64 rows per wave: a K or V^T fragment read from LDS then feeds two
+// MFMAs (two 32-row query blocks) instead of one. With 32 rows per wave the
+// transposing V^T reads alone (ds_read_b64_tr_b16 moves half the bytes of a
+// ds_read_b128 per instruction) cap the PV product below the MFMA rate. The
+// price is registers: O^T (128) and Q^T (64) live in AGPRs, S, P and the
+// fragment rings in VGPRs, one wave per SIMD.
+//
+// Work decomposition: a workgroup takes one 64-token query tile, one KV head
+// and HP of its query heads (one wave per head), and stages each 64-key K and
+// V tile once for all HP waves. HP = 4 runs one workgroup per CU, HP = 2 two.
+// The KV head varies fastest over blockIdx, so with 8 KV heads each XCD (the
+// dispatcher deals workgroups round-robin to the 8 XCDs) serves one KV head
+// from its own L2. Query tiles arrive longest first (the builder's work list).
+//
+// The key-tile loop is one inline-assembly block (attn_loop.inc, written by
+// gen_attn_loop.py, which documents the register map and the pipeline). The
+// compiler cannot keep this split of AGPR and VGPR state apart by itself: it
+// moves the accumulators between the two files on every step.
+//
+// Layouts (shared with the LDS-direct loads the block issues):
+//   LDS: the K stages, then the V stages, 16 KB each, 64 keys x 256-byte rows; chunk c (16 bytes) of K row r sits in slot c ^ (r & 15),
+//   of V row r in slot c ^ 4 (r & 3), so the K reads (ds_read_b128, 16
+//   consecutive keys at one chunk) and the transposing V reads are free of
+//   bank conflicts.
+//   MFMA v_mfma_f32_32x32x16_bf16: S^T = K Q^T with the keys on the rows, so a
+//   lane owns one query column and P^T leaves the accumulator already in the
+//   B-operand layout of O^T += V^T P^T; V^T comes from ds_read_b64_tr_b16 in
+//   the key order the accumulator implies (keys {4g..4g+3, 8+4g..8+4g+3} of a
+//   16-key step in the eight slots of lane group g).
+#include "attn_loop.inc"
+#include "gfx950_util.h"
+#include "mis_internal.h"
+
+namespace mis {
+namespace {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+
+constexpr int D = 128;
+constexpr int BM = kAttnBlockM;  // query tokens per workgroup (and per wave)
+constexpr int BN = kAttnBlockN;  // keys per LDS tile
+constexpr int TILE = BN * D;     // bf16 elements of one K or V stage
+constexpr float kLog2e = 1.4426950408889634f;
+static_assert(BM == 64 && BN == 64, "the loop block is written for 64 x 64 tiles");
+
+// Scalars and per-lane values the loop block reads (names as in the block).
+struct LoopArgs {
+  uint32_t ka[8];   // LDS byte address of this lane's K fragment slot, per 16-dim step
+  uint32_t va[4];   // LDS byte address of this lane's V^T read, per 32-dim block
+  uint32_t ko[4];   // global byte offset of this lane's K chunk in a tile, per DMA row group
+  uint32_t vo;      // same for V (its swizzle does not depend on the row group)
+  int rjt[2];       // last visible key of the lane's two query rows, minus 4g
+  int rjb[2];       // first key of the rows' own item (0 for prefix rows), minus 4g
+  int rlq;          // prefix length minus 4g
+  int nvis, a_end, b_start, a_full;
+  uint32_t kb_lo, kb_hi, vb_lo, vb_hi;  // this KV head's K and V at the request start
+  uint32_t rb64, rb4, nrec;             // 64 and 4 token rows in bytes; descriptor range
+  uint32_t wsoff, wlds;                 // this wave's first DMA row: global offset, LDS address
+  float c;                              // softmax scale * log2(e)
+};
+
+#define MIS_ATTN_LOOP_OPERANDS                                                                                      \
+  : [o0] "={a[0:31]}"(o0), [o1] "={a[32:63]}"(o1), [o2] "={a[64:95]}"(o2), [o3] "={a[96:127]}"(o3),              \
+    [l0] "=v"(l0), [l1] "=v"(l1)                                                                                    \
+  : [q0] "{a[128:159]}"(q0), [q1] "{a[160:191]}"(q1), [ka0] "v"(x.ka[0]), [ka1] "v"(x.ka[1]),                    \
+    [ka2] "v"(x.ka[2]), [ka3] "v"(x.ka[3]), [ka4] "v"(x.ka[4]), [ka5] "v"(x.ka[5]), [ka6] "v"(x.ka[6]),            \
+    [ka7] "v"(x.ka[7]), [va0] "v"(x.va[0]), [va1] "v"(x.va[1]), [va2] "v"(x.va[2]), [va3] "v"(x.va[3]),            \
+    [ko0] "v"(x.ko[0]), [ko1] "v"(x.ko[1]), [ko2] "v"(x.ko[2]), [ko3] "v"(x.ko[3]), [vo] "v"(x.vo),                \
+    [rjt0] "v"(x.rjt[0]), [rjt1] "v"(x.rjt[1]), [rjb0] "v"(x.rjb[0]), [rjb1] "v"(x.rjb[1]), [rlq] "v"(x.rlq),     \
+    [nvis] "s"(x.nvis), [a_end] "s"(x.a_end), [b_start] "s"(x.b_start), [a_full] "s"(x.a_full),                   \
+    [kb_lo] "s"(x.kb_lo), [kb_hi] "s"(x.kb_hi), [vb_lo] "s"(x.vb_lo), [vb_hi] "s"(x.vb_hi), [rb64] "s"(x.rb64),    \
+    [rb4] "s"(x.rb4), [nrec] "s"(x.nrec), [wsoff] "s"(x.wsoff), [wlds] "s"(x.wlds), [c] "s"(x.c)                  \
+  : MIS_ATTN_LOOP_CLOBBERS
+
+// Runs the whole key-tile loop; O^T (unnormalised) and the lane's partial row
+// sums come back. DPW = LDS-direct loads per wave, tile and operand (16 / HP).
+template <int DPW>
+__device__ __forceinline__ void attn_loop(const LoopArgs &x, const f32x32 &q0, const f32x32 &q1, f32x32 &o0,
+                                          f32x32 &o1, f32x32 &o2, f32x32 &o3, float &l0, float &l1) {
+  static_assert(DPW == 4 || DPW == 8, "loop block generated for 2 or 4 heads per workgroup");
+  // The block writes M0 (the LDS address of its loads). Clang warns that a
+  // reserved register is listed as clobbered; the compiler sets M0 itself
+  // before each of its own uses, and none follows the block.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  if constexpr (DPW == 4)
+    asm volatile(MIS_ATTN_LOOP_TEXT_DPW4 MIS_ATTN_LOOP_OPERANDS);
+  else
+    asm volatile(MIS_ATTN_LOOP_TEXT_DPW8 MIS_ATTN_LOOP_OPERANDS);
+#pragma clang diagnostic pop
+}
+
+// K/V stages of the ring: three when one workgroup holds the CU (HP = 4, 96
+// KB of LDS), two when two workgroups share it (HP = 2, 64 KB each).
+template <int HP>
+constexpr int kStages = HP == 4 ? 3 : 2;
+
+template <int HP>
+__global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
+    const int32_t *__restrict__ work, const int32_t *__restrict__ cu_seqlens,
+    const int32_t *__restrict__ prefix_lens, const int32_t *__restrict__ cu_tiles,
+    const int8_t *__restrict__ tile_class, const int32_t *__restrict__ item_id,
+    const int32_t *__restrict__ item_begin, const __bf16 *__restrict__ q,
+    const __bf16 *__restrict__ k, const __bf16 *__restrict__ v, __bf16 *__restrict__ o, int hq,
+    int hkv, float c, int items_only) {
+  constexpr int ROWS_PER_WAVE = BN / HP;  // tile rows each wave loads
+  constexpr int STAGES = kStages<HP>;
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * STAGES * TILE];  // K stages, then V stages
+
+  const int gsz = hq / hkv;
+  const int groups = gsz / HP;
+  const int kvh = blockIdx.x % hkv;
+  const int rest = blockIdx.x / hkv;
+  const int hc = rest % groups;
+  const int w = rest / groups;
+
+  const int r = work[4 * w + 0];
+  const int qt = work[4 * w + 1];
+  const int a_end = work[4 * w + 2];  // prefix key tiles [0, a_end)
+  const int b_lo = work[4 * w + 3];   // first key tile of the own-item range
+  const int base = cu_seqlens[r];
+  const int Tr = cu_seqlens[r + 1] - base;
+  const int lq = prefix_lens[r];
+  // Appending items to a cached prefix: a query tile that holds prefix rows
+  // only has nothing to compute (the whole workgroup leaves together).
+  if (items_only && qt * BM + BM <= lq) return;
+  const int nkt = (Tr + BN - 1) / BN;
+  const int j1 = min(Tr, qt * BM + BM);
+  const int b_hi = (j1 + BN - 1) / BN;
+  const int b_start = max(b_lo, a_end);
+  const int n_visit = a_end + (b_hi - b_start);
+  const int cls_base = cu_tiles[r] + qt * nkt;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 5;
+  const int ql = lane & 31;
+  const int head = kvh * gsz + hc * HP + wave;
+
+  LoopArgs x;
+  x.nvis = n_visit;
+  x.a_end = a_end;
+  x.b_start = b_start;
+  // Visits before a_full are fully visible tiles (class 2) that end inside
+  // the request; the mask runs on every visit from a_full on.
+  {
+    int first = n_visit;
+#pragma unroll 4
+    for (int i0 = 0; i0 < n_visit; i0 += 64) {
+      const int idx = i0 + lane;
+      if (idx < n_visit) {
+        const int kt = idx < a_end ? idx : b_start + (idx - a_end);
+        if ((tile_class[cls_base + kt] != 2) | (kt * BN + BN > Tr)) first = min(first, idx);
+      }
+    }
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) first = min(first, __shfl_xor(first, s));
+    x.a_full = __builtin_amdgcn_readfirstlane(first);
+  }
+
+  // Mask bounds of the lane's two query rows (j = query block * 32 + lane % 32);
+  // the lane's keys in a sub-tile are key0 + 8 (a / 4) + a % 4 + 4 g.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int j = qt * BM + 32 * qb + ql;
+    const int jb = (j < Tr && j >= lq) ? item_begin[item_id[base + j]] - base : 0;
+    x.rjt[qb] = min(j, Tr - 1) - 4 * g;
+    x.rjb[qb] = jb - 4 * g;
+  }
+  x.rlq = lq - 4 * g;
+
+  const int64_t q_stride = int64_t(hq) * D;
+  const int64_t kv_stride = int64_t(hkv) * D;
+  const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
+
+  // The V stages start as zeros: rows past the request end are not written
+  // by the loads, and the first PV step multiplies a zero P with the last stage.
+  for (int i = tid; i < STAGES * TILE / 8; i += 64 * HP)
+    *reinterpret_cast<uint4 *>(&smem[STAGES * TILE + i * 8]) = make_uint4(0, 0, 0, 0);
+
+  // Q^T operands of the two query blocks; rows past the request end read as zeros.
+  f32x32 qv[2];
+  {
+    const uint32_t q_bytes = uint32_t(Tr) * uint32_t(q_stride) * 2u - uint32_t(head) * D * 2u;
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(q + int64_t(base) * q_stride + int64_t(head) * D), 0, q_bytes, kRsrcWord3);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const uint32_t qo = uint32_t(qt * BM + 32 * qb + ql) * uint32_t(q_stride) * 2u + 16u * g;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const f32x4 f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qo + 32u * kk, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[qb][4 * kk + e] = f[e];
+      }
+    }
+  }
+
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t vlds0 = lds0 + uint32_t(STAGES * TILE * 2);  // start of the V stages
+  // K fragment of 16-dim step kk: key ql (+32 for the second key block), chunk 2 kk + g.
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) x.ka[kk] = lds0 + uint32_t(ql) * 256u + 16u * uint32_t((2 * kk + g) ^ (ql & 15));
+  // V^T reads: in a 16-lane group G, lanes 4e..4e+3 read key 4 (G / 2) + e (and
+  // eight rows further), dims 32 db + 16 (G % 2) + 4 (lane % 4); the transpose
+  // hands lane i of the group dim 32 db + 16 (G % 2) + i of four keys.
+  {
+    const int G = lane >> 4, e = (lane >> 2) & 3, qd = lane & 3;
+    const int key = 4 * (G >> 1) + e;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int chunk = 4 * db + 2 * (G & 1) + (qd >> 1);
+      x.va[db] = vlds0 + uint32_t(key) * 256u + 16u * uint32_t(chunk ^ (4 * (key & 3))) + 8u * uint32_t(qd & 1);
+    }
+  }
+  // LDS-direct loads: instruction i of a wave covers tile rows ROWS_PER_WAVE *
+  // wave + 4 i + lane / 16, LDS slot lane % 16, so the lane fetches global
+  // chunk slot ^ swizzle(row); ROWS_PER_WAVE is a multiple of 16, so the K
+  // swizzle depends on i % 4 and lane / 16 only.
+  {
+    const int rl = lane >> 4, slot = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x.ko[i] = uint32_t(rl) * kv_row_bytes + 16u * uint32_t(slot ^ ((4 * i + rl) & 15));
+    x.vo = uint32_t(rl) * kv_row_bytes + 16u * uint32_t(slot ^ (4 * (rl & 3)));
+  }
+  const uint64_t kb = reinterpret_cast<uint64_t>(k + int64_t(base) * kv_stride + int64_t(kvh) * D);
+  const uint64_t vb = reinterpret_cast<uint64_t>(v + int64_t(base) * kv_stride + int64_t(kvh) * D);
+  x.kb_lo = uint32_t(kb);
+  x.kb_hi = uint32_t(kb >> 32);
+  x.vb_lo = uint32_t(vb);
+  x.vb_hi = uint32_t(vb >> 32);
+  x.rb64 = 64u * kv_row_bytes;
+  x.rb4 = 4u * kv_row_bytes;
+  // A tile descriptor starting at key k0 covers nrec - k0 * row bytes: up to
+  // this head's last key of the request, so rows past the end read nothing.
+  x.nrec = uint32_t(Tr) * kv_row_bytes - uint32_t(kvh) * D * 2u;
+  const uint32_t wrow = uint32_t(ROWS_PER_WAVE * wave);
+  x.wsoff = wrow * kv_row_bytes;
+  x.wlds = lds0 + wrow * 256u;
+  x.c = c;
+
+  __syncthreads();  // V zero fill done before any load lands in LDS
+
+  f32x32 o0, o1, o2, o3;
+  float l0, l1;
+  attn_loop<BN / HP / 4>(x, qv[0], qv[1], o0, o1, o2, o3, l0, l1);
+
+  // O^T accumulator element a of lane l: dim 8 (a / 4) + 4 g + a % 4 of the
+  // 32-dim block, query row l % 32 of the block.
+  const float inv0 = 1.0f / (l0 + __shfl_xor(l0, 32));
+  const float inv1 = 1.0f / (l1 + __shfl_xor(l1, 32));
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int j = qt * BM + 32 * qb + ql;
+    if (j >= Tr) continue;
+    const float inv = qb ? inv1 : inv0;
+    __bf16 *op = o + int64_t(base + j) * q_stride + int64_t(head) * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const f32x32 &ob = qb ? (db < 2 ? o2 : o3) : (db < 2 ? o0 : o1);
+      const int off = 16 * (db & 1);
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = __bf16(ob[off + 4 * a4 + e] * inv);
+        *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * a4 + 4 * g) = ov;
+      }
+    }
+  }
+}
+
+template <int HP>
+hipError_t launch_pipe(const mis_segments &seg, const void *q, const void *k, const void *v, void *o, int hq,
+                       int hkv, float c, int items_only, hipStream_t st) {
+  const int64_t blocks = int64_t(seg.num_work) * hq / HP;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  attn_pipe_kernel<HP><<<dim3(unsigned(blocks)), 64 * HP, 0, st>>>(
+      seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.item_id, seg.item_begin,
+      static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k), static_cast<const __bf16 *>(v),
+      static_cast<__bf16 *>(o), hq, hkv, c, items_only);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_bf16_pipe(const mis_segments &seg, const void *q, const void *k, const void *v, void *o,
+                                      int hq, int hkv, float scale, int items_only, hipStream_t st) {
+  const int gsz = hq / hkv;
+  if (gsz % 2 != 0) return hipErrorInvalidValue;
+  const float c = scale * kLog2e;
+  // 4 heads per workgroup share each staged K/V tile among 4 waves (one
+  // workgroup per CU); 2 heads run two workgroups per CU.
+  if (gsz % 4 == 0) return launch_pipe<4>(seg, q, k, v, o, hq, hkv, c, items_only, st);
+  return launch_pipe<2>(seg, q, k, v, o, hq, hkv, c, items_only, st);
+}
+
+}  // namespace mis

@@ -39,6 +39,12 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
                                  const void *v, void *o, int hq, int hkv, int d, float scale,
                                  int items_only, hipStream_t stream);
 
+// 64 query rows per wave, software-pipelined key-tile loop (even GQA group
+// sizes, head_dim 128); launch_attention_bf16 dispatches to it.
+hipError_t launch_attention_bf16_pipe(const mis_segments &seg, const void *q, const void *k,
+                                      const void *v, void *o, int hq, int hkv, float scale,
+                                      int items_only, hipStream_t stream);
+
 // Inverse frequencies theta^(-2i/D) of the rotary embedding, i < D/2.
 struct RopeFreq {
   double inv[64];
