@@ -59,6 +59,8 @@
 // share it); the O rescale is skipped when no lane of the wave raised it.
 // Row sums add the bf16-rounded P (the values the PV product uses), two per
 // v_dot2_f32_bf16.
+#include <cstdlib>
+#include <cstring>
 #include <utility>
 
 #include "gfx950_util.h"
@@ -438,14 +440,28 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
                                  int items_only, hipStream_t st) {
   if (d != D) return hipErrorInvalidValue;
   const int gsz = hq / hkv;
-  // Even group sizes (every GQA shape of the workloads) take the kernel with
-  // 64 query rows per wave; odd ones (MHA included) this one, one head per
-  // workgroup.
-  if (gsz % 2 == 0) return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, st);
   const float c = scale * kLog2e;
-  return launch_variant<2, 1>(seg, static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k),
-                              static_cast<const __bf16 *>(v), static_cast<__bf16 *>(o), hq, hkv, c, items_only,
-                              st);
+  const __bf16 *qp = static_cast<const __bf16 *>(q);
+  const __bf16 *kp = static_cast<const __bf16 *>(k);
+  const __bf16 *vp = static_cast<const __bf16 *>(v);
+  __bf16 *op = static_cast<__bf16 *>(o);
+  // Long runs of work (GQA groups of 4 or more and at least 8 four-head
+  // workgroups per CU) take the kernel with 64 query rows per wave: one wave
+  // per SIMD, so it cannot hide the fixed cost of starting a query tile
+  // behind another workgroup, but its key-tile loop is faster. Otherwise this
+  // kernel (two waves per SIMD): 2 token blocks x 2 heads of one KV head, or
+  // one head for odd group sizes.
+  // MIS_ATTENTION_KERNEL=pipe or =classic forces one of the two (tests run
+  // every shape through both); the pipelined one needs an even group size.
+  const char *force = std::getenv("MIS_ATTENTION_KERNEL");
+  const bool want_pipe = force && std::strcmp(force, "pipe") == 0;
+  const bool want_classic = force && std::strcmp(force, "classic") == 0;
+  const bool pipe_fits = gsz % 2 == 0;
+  const bool pipe_pays = gsz % 4 == 0 && int64_t(seg.num_work) * (hq / 4) >= 8 * int64_t(device_cus());
+  if (pipe_fits && (want_pipe || (pipe_pays && !want_classic)))
+    return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, st);
+  if (gsz % 2 == 0) return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
+  return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
 }
 
 }  // namespace mis

@@ -83,8 +83,8 @@ struct LoopArgs {
     [rb4] "s"(x.rb4), [nrec] "s"(x.nrec), [wsoff] "s"(x.wsoff), [wlds] "s"(x.wlds), [c] "s"(x.c)                  \
   : MIS_ATTN_LOOP_CLOBBERS
 
-// Runs the whole key-tile loop; O^T (unnormalised) and the lane's partial row
-// sums come back. DPW = LDS-direct loads per wave, tile and operand (16 / HP).
+// Runs the whole key-tile loop; O^T (unnormalised) and the row sums of the
+// lane's two query rows come back. DPW = LDS-direct loads per wave, tile and operand (16 / HP).
 template <int DPW>
 __device__ __forceinline__ void attn_loop(const LoopArgs &x, const f32x32 &q0, const f32x32 &q1, f32x32 &o0,
                                           f32x32 &o1, f32x32 &o2, f32x32 &o3, float &l0, float &l1) {
@@ -149,6 +149,25 @@ __global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
   const int ql = lane & 31;
   const int head = kvh * gsz + hc * HP + wave;
 
+  const int64_t q_stride = int64_t(hq) * D;
+  // Q^T operands of the two query blocks; rows past the request end read as zeros.
+  f32x32 qv[2];
+  {
+    const uint32_t q_bytes = uint32_t(Tr) * uint32_t(q_stride) * 2u - uint32_t(head) * D * 2u;
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(q + int64_t(base) * q_stride + int64_t(head) * D), 0, q_bytes, kRsrcWord3);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const uint32_t qo = uint32_t(qt * BM + 32 * qb + ql) * uint32_t(q_stride) * 2u + 16u * g;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const f32x4 f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qo + 32u * kk, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[qb][4 * kk + e] = f[e];
+      }
+    }
+  }
+
   LoopArgs x;
   x.nvis = n_visit;
   x.a_end = a_end;
@@ -181,7 +200,6 @@ __global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
   }
   x.rlq = lq - 4 * g;
 
-  const int64_t q_stride = int64_t(hq) * D;
   const int64_t kv_stride = int64_t(hkv) * D;
   const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
 
@@ -189,24 +207,6 @@ __global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
   // by the loads, and the first PV step multiplies a zero P with the last stage.
   for (int i = tid; i < STAGES * TILE / 8; i += 64 * HP)
     *reinterpret_cast<uint4 *>(&smem[STAGES * TILE + i * 8]) = make_uint4(0, 0, 0, 0);
-
-  // Q^T operands of the two query blocks; rows past the request end read as zeros.
-  f32x32 qv[2];
-  {
-    const uint32_t q_bytes = uint32_t(Tr) * uint32_t(q_stride) * 2u - uint32_t(head) * D * 2u;
-    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16 *>(q + int64_t(base) * q_stride + int64_t(head) * D), 0, q_bytes, kRsrcWord3);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const uint32_t qo = uint32_t(qt * BM + 32 * qb + ql) * uint32_t(q_stride) * 2u + 16u * g;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const f32x4 f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qo + 32u * kk, 0, 0));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qv[qb][4 * kk + e] = f[e];
-      }
-    }
-  }
 
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t vlds0 = lds0 + uint32_t(STAGES * TILE * 2);  // start of the V stages
@@ -258,9 +258,10 @@ __global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
   attn_loop<BN / HP / 4>(x, qv[0], qv[1], o0, o1, o2, o3, l0, l1);
 
   // O^T accumulator element a of lane l: dim 8 (a / 4) + 4 g + a % 4 of the
-  // 32-dim block, query row l % 32 of the block.
-  const float inv0 = 1.0f / (l0 + __shfl_xor(l0, 32));
-  const float inv1 = 1.0f / (l1 + __shfl_xor(l1, 32));
+  // 32-dim block, query row l % 32 of the block. l0 and l1 are the full row
+  // sums of the lane's two query rows.
+  const float inv0 = 1.0f / l0;
+  const float inv1 = 1.0f / l1;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int j = qt * BM + 32 * qb + ql;
@@ -302,7 +303,7 @@ hipError_t launch_attention_bf16_pipe(const mis_segments &seg, const void *q, co
   if (gsz % 2 != 0) return hipErrorInvalidValue;
   const float c = scale * kLog2e;
   // 4 heads per workgroup share each staged K/V tile among 4 waves (one
-  // workgroup per CU); 2 heads run two workgroups per CU.
+  // workgroup per CU, a 3-stage ring); 2 heads run two workgroups per CU.
   if (gsz % 4 == 0) return launch_pipe<4>(seg, q, k, v, o, hq, hkv, c, items_only, st);
   return launch_pipe<2>(seg, q, k, v, o, hq, hkv, c, items_only, st);
 }

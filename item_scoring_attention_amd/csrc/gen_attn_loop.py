@@ -22,20 +22,18 @@ the sub-tile is taken, O and the row sum are rescaled and P is recomputed.
 Any m that was ever a real maximum keeps the result exact, because O and the
 row sum are scaled by the same exp2(-m).
 
-Register map (physical, clobbered by the block):
+Register map (physical, clobbered by the block; see the constants below):
   v[0:31]    S_A   (S^T of a sub-tile, 2 query blocks x 16 fp32)
   v[32:63]   S_B
   v[64:79]   P_A   (P^T bf16, [qb][ks] 4 dwords each)
   v[80:95]   P_B
-  v[96:107]  K fragment ring (3 x 4)
-  v[108:119] V^T fragment ring (3 x 4)
-  v[120:127] exp temporaries
-  v[128:135] mask / rescale temporaries
-  v136, v137 running maxima m (exp2 domain), v138, v139 row sums l,
-  v140, v141 partial row sums of the current sub-tile (v143, v144 second
-             chains), v142 -inf
+  then the K and V^T fragment rings (RING x 4 each), exp temporaries,
+  mask / rescale temporaries, m, the overflow-check maxima and bf16 ones
   a[0:127]   O^T accumulators [qb][db] (operands, pinned)
   a[128:191] Q^T fragments [qb][dstep] (operands, pinned)
+  a[192:223] row sums: 1^T P^T on the matrix cores, so they add exactly the
+             bf16 P that O^T += V^T P^T uses (every row of the 32 x 32
+             accumulator holds the sums; the block returns element 0)
 """
 from __future__ import annotations
 
@@ -64,16 +62,17 @@ def v_lds(stage, stages):
     return STAGE_BYTES * (stages + stage)
 
 S_A, S_B, P_A, P_B = 0, 32, 64, 80
-KB = (96, 100, 104)
-VB = (108, 112, 116)
-E0 = 120
-X0 = 128
-VM = (136, 137)
-VL = (138, 139)
-VT = (140, 141)
-VNINF = 142
-VT2 = (143, 144)
-NUM_V = 145
+RING = 4  # K and V^T fragments in flight (each ring slot is 4 VGPRs)
+KB = tuple(96 + 4 * i for i in range(RING))
+VB = tuple(96 + 4 * RING + 4 * i for i in range(RING))
+E0 = 96 + 8 * RING          # 16 exp temporaries (8 pairs in flight)
+X0 = E0 + 16                # 8 mask / rescale temporaries
+VM = (X0 + 8, X0 + 9)       # running maxima m (exp2 domain)
+VMX = (X0 + 10, X0 + 11)    # largest P of the current sub-tile (overflow check)
+VNINF = X0 + 12             # -inf
+ONES = X0 + 16              # 4 VGPRs of bf16 ones: the A operand of the row-sum MFMAs
+NUM_V = X0 + 20
+LS = 192                    # a[192:223]: row-sum accumulators [qb], 16 AGPRs each
 
 # SGPRs used inside the block
 S_T = 40      # visit index of the current tile pair (even)
@@ -89,10 +88,16 @@ S_SO = 60     # soffset of a DMA instruction
 S_OFF = 61
 S_NV1 = 62    # scratch
 S_LAST = 63
-S_NL = 46     # LDS-direct loads issued at the previous barrier (still allowed in flight)
-SGPRS = list(range(40, 64))
+S_VRSRC = 64  # V buffer descriptor s[64:67]
+S_VSO = 68    # soffset of a V load
+SGPRS = list(range(40, 72))
 
 MFMA = "v_mfma_f32_32x32x16_bf16"
+# VALU cycles placed after each MFMA (one v_mfma_f32_32x32x16_bf16 keeps the
+# matrix pipe busy for 32 cycles; an exp costs about 10 issue cycles, other
+# VALU 4) and before the first one (while the first K fragment arrives).
+SLOT_BUDGET = 24
+HEAD_BUDGET = 16
 
 
 def vr(a, n=1):
@@ -125,78 +130,102 @@ class Block:
         idx = max(i for i, t in enumerate(self.ds) if t == tag)
         if idx < self.done:
             return
-        after = len(self.ds) - idx - 1
-        assert after <= 15, "lgkmcnt holds at most 15 outstanding operations"
-        self.emit(f"s_waitcnt lgkmcnt({after})")
-        self.done = idx + 1
+        # lgkmcnt(n) leaves at most n operations in flight; with more than 15
+        # issued after the target, waiting for 15 still covers the target
+        n = min(len(self.ds) - idx - 1, 15)
+        self.emit(f"s_waitcnt lgkmcnt({n})")
+        self.done = len(self.ds) - n
 
     def reset_ds(self):
         self.ds = []
         self.done = 0
 
 
-def softmax_ops(s_cur: int, p_cur: int, c: str) -> list[str]:
-    """VALU stream turning S_cur into P_cur and the partial row sums VT.
+def softmax_graph(s_cur: int, p_cur: int, c: str):
+    """VALU work turning S_cur into P_cur (bf16) and the largest P per row, as
+    (text, cost, deps) nodes. Pair i (qb = i // 8, elements 2pi, 2pi+1):
+    two FMAs (c s - m), two exps, a convert into dword pi of P_cur[qb] and a
+    max3 into VMX[qb]. Pair i uses exp temporaries E0 + 2 (i % 8), so pair
+    i + 8 waits for pair i's convert and max (write after read). The row
+    sums are not formed here: 1^T P^T runs on the matrix cores."""
+    nodes = []
 
-    Pair i (qb = i // 8, elements 2pi, 2pi+1) writes dword pi of P_cur[qb]:
-    two FMAs (c s - m), two exps, one convert to bf16, then the two rounded
-    values are unpacked (shift, mask) and added to the row-sum chains VT[qb]
-    and VT2[qb], so the sums hold exactly the P that the PV product uses.
-    (v_dot2_f32_bf16 would add a rounded pair in one instruction, but it does
-    not run beside the MFMAs.) The unpack and adds of pair i-1 are placed
-    inside pair i, so no instruction reads an exp result it directly follows
-    and no chain add waits on the instruction before it."""
-    ops = []
+    def add(text, cost, deps):
+        nodes.append((text, cost, tuple(deps)))
+        return len(nodes) - 1
 
-    def tail(i):
-        qb, pi = divmod(i, 8)
-        pd = p_cur + 8 * qb + pi
-        ra, rb = X0 + 4 + 2 * (i % 2), X0 + 5 + 2 * (i % 2)
-        unpack = [f"v_lshlrev_b32 {vr(ra)}, 16, {vr(pd)}",
-                  f"v_and_b32 {vr(rb)}, 0xffff0000, {vr(pd)}"]
-        if pi == 0:
-            adds = [f"v_mov_b32 {vr(VT[qb])}, {vr(ra)}", f"v_mov_b32 {vr(VT2[qb])}, {vr(rb)}"]
-        else:
-            adds = [f"v_add_f32 {vr(VT[qb])}, {vr(VT[qb])}, {vr(ra)}",
-                    f"v_add_f32 {vr(VT2[qb])}, {vr(VT2[qb])}, {vr(rb)}"]
-        return unpack, adds
-
+    last_max = {0: None, 1: None}
+    done_pair = {}
     for i in range(16):
         qb, pi = divmod(i, 8)
-        ea = E0 + 2 * (i % 4)
+        ea = E0 + 2 * (i % 8)
         eb = ea + 1
         sa = s_cur + 16 * qb + 2 * pi
         m = VM[qb]
-        ops += [f"v_fma_f32 {vr(ea)}, {vr(sa)}, {c}, -{vr(m)}",
-                f"v_fma_f32 {vr(eb)}, {vr(sa + 1)}, {c}, -{vr(m)}",
-                f"v_exp_f32 {vr(ea)}, {vr(ea)}"]
-        prev = tail(i - 1) if i else None
-        if prev:
-            ops += prev[0]
-        ops.append(f"v_exp_f32 {vr(eb)}, {vr(eb)}")
-        ops += prev[1] if prev else ["s_nop 1"]
-        ops.append(f"v_cvt_pk_bf16_f32 {vr(p_cur + 8 * qb + pi)}, {vr(ea)}, {vr(eb)}")
-    unpack, adds = tail(15)
-    ops += unpack + adds
-    ops += [f"v_add_f32 {vr(VT[q])}, {vr(VT[q])}, {vr(VT2[q])}" for q in range(2)]
+        war = done_pair.get(i - 8, ())
+        fa = add(f"v_fma_f32 {vr(ea)}, {vr(sa)}, {c}, -{vr(m)}", 4, war)
+        fb = add(f"v_fma_f32 {vr(eb)}, {vr(sa + 1)}, {c}, -{vr(m)}", 4, war)
+        xa = add(f"v_exp_f32 {vr(ea)}, {vr(ea)}", 10, [fa])
+        xb = add(f"v_exp_f32 {vr(eb)}, {vr(eb)}", 10, [fb])
+        cv = add(f"v_cvt_pk_bf16_f32 {vr(p_cur + 8 * qb + pi)}, {vr(ea)}, {vr(eb)}", 4, [xa, xb])
+        lm = last_max[qb]
+        mx = add(f"v_max_f32 {vr(VMX[qb])}, {vr(ea)}, {vr(eb)}" if lm is None else
+                 f"v_max3_f32 {vr(VMX[qb])}, {vr(VMX[qb])}, {vr(ea)}, {vr(eb)}", 4,
+                 [xa, xb] + ([] if lm is None else [lm]))
+        last_max[qb] = mx
+        done_pair[i] = (cv, mx)
+    return nodes
+
+
+def softmax_ops(s_cur: int, p_cur: int, c: str) -> list[str]:
+    """The softmax work in a plain order for the slow path: nodes in creation
+    order, with one independent instruction (or a nop) after every exp."""
+    ops = []
+    for text, _, deps in softmax_graph(s_cur, p_cur, c):
+        if ops and ops[-1].startswith("v_exp_f32") and text.split()[0] != "v_exp_f32":
+            ops.append("s_nop 1")
+        ops.append(text)
     return ops
 
 
-def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c):
-    """One pipelined sub-tile: QK(next) + PV(prev) MFMAs interleaved with softmax(cur)."""
+def schedule(nodes, slots: int, budget: int, head_budget: int):
+    """Place every node in one of slots + 1 groups (group 0 runs before the
+    first MFMA, group k after MFMA k - 1) so that a node lands in a later
+    group than each node it depends on (at least one MFMA between producer
+    and consumer, which covers the exp latency and the trans-use hazard) and
+    no group exceeds its cycle budget when it can be helped."""
+    group = [0] * len(nodes)
+    load = [0] * (slots + 1)
+    out = [[] for _ in range(slots + 1)]
+    for n, (text, cost, deps) in enumerate(nodes):
+        g = max((group[d] + 1 for d in deps), default=0)
+        cap = lambda k: head_budget if k == 0 else budget
+        while g < slots and load[g] + cost > cap(g):
+            g += 1
+        g = min(g, slots)
+        group[n] = g
+        load[g] += cost
+        out[g].append(text)
+    return out
+
+
+def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c, side=()):
+    """One pipelined sub-tile: QK(next) + PV(prev) MFMAs interleaved with softmax(cur).
+
+    `side` holds small instruction groups (the next tiles' LDS-direct loads)
+    issued one after each MFMA from the second on, so their issue cost hides
+    under the matrix pipe."""
     b.reset_ds()
-    flat = softmax_ops(s_cur, p_cur, c)
-    head = 6  # VALU issued before the first MFMA (covers the first K read)
-    per = -(-(len(flat) - head) // 32)
-    valu = [flat[:head]] + [flat[head + per * k: head + per * (k + 1)] for k in range(32)]
+    side = list(side)
+    valu = schedule(softmax_graph(s_cur, p_cur, c), 32, SLOT_BUDGET, HEAD_BUDGET)
     vi = 0
 
     def k_read(ds):
-        b.ds_op(f"k{ds}", f"ds_read_b128 {vr(KB[ds % 3], 4)}, %[ka{ds}] offset:{koff}")
+        b.ds_op(f"k{ds}", f"ds_read_b128 {vr(KB[ds % RING], 4)}, %[ka{ds}] offset:{koff}")
 
     def v_read(f):
         ks, db = divmod(f, 4)
-        buf = VB[f % 3]
+        buf = VB[f % RING]
         off = voff + 4096 * ks
         b.ds_op(f"v{f}", f"ds_read_b64_tr_b16 {vr(buf, 2)}, %[va{db}] offset:{off}")
         b.ds_op(f"v{f}", f"ds_read_b64_tr_b16 {vr(buf + 2, 2)}, %[va{db}] offset:{off + 2048}")
@@ -208,9 +237,9 @@ def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c):
                 b.emit(ln)
             vi += 1
 
-    for ds in range(3):
+    for ds in range(RING):
         k_read(ds)
-    for f in range(3):
+    for f in range(RING):
         v_read(f)
     valu_group()
     for slot in range(32):
@@ -219,18 +248,28 @@ def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c):
             b.wait_ds(f"k{ds}")
             acc = vr(s_next + 16 * qb, 16)
             src_c = "0" if ds == 0 else acc
-            b.emit(f"{MFMA} {acc}, {vr(KB[ds % 3], 4)}, {ar(128 + 32 * qb + 4 * ds, 4)}, {src_c}")
-            if qb == 1 and ds + 3 < 8:
-                k_read(ds + 3)
+            b.emit(f"{MFMA} {acc}, {vr(KB[ds % RING], 4)}, {ar(128 + 32 * qb + 4 * ds, 4)}, {src_c}")
+            if qb == 1 and ds + RING < 8:
+                k_read(ds + RING)
         else:
             f, qb = divmod(slot - 16, 2)
             ks, db = divmod(f, 4)
             b.wait_ds(f"v{f}")
             o = ar(16 * (4 * qb + db), 16)
-            b.emit(f"{MFMA} {o}, {vr(VB[f % 3], 4)}, {vr(p_prev + 8 * qb + 4 * ks, 4)}, {o}")
-            if qb == 1 and f + 3 < 8:
-                v_read(f + 3)
+            b.emit(f"{MFMA} {o}, {vr(VB[f % RING], 4)}, {vr(p_prev + 8 * qb + 4 * ks, 4)}, {o}")
+            if qb == 1 and f + RING < 8:
+                v_read(f + RING)
+            if qb == 1 and db == 3:
+                for q in range(2):
+                    ls = ar(LS + 16 * q, 16)
+                    b.emit(f"{MFMA} {ls}, {vr(ONES, 4)}, {vr(p_prev + 8 * q + 4 * ks, 4)}, {ls}")
+        if slot >= 1 and side:
+            for ln in side.pop(0):
+                b.emit(ln)
         valu_group()
+    for g in side:
+        for ln in g:
+            b.emit(ln)
     while vi < len(valu):
         valu_group()
 
@@ -256,7 +295,7 @@ def mask_code(b: Block, s_cur: int, half: int, skip_label: str):
 
 
 def slow_path(b: Block, s_cur, p_cur, c, label, ret):
-    """Raise m to the sub-tile maximum, rescale O and l, recompute P and the sums."""
+    """Raise m to the sub-tile maximum, rescale O and the row sums, recompute P."""
     b.emit(f"{label}:")
     b.emit("s_nop 7")
     b.emit("s_nop 7")
@@ -279,10 +318,8 @@ def slow_path(b: Block, s_cur, p_cur, c, label, ret):
         b.emit(f"v_sub_f32 {vr(al)}, {vr(VM[qb])}, {vr(x)}")
         b.emit(f"v_exp_f32 {vr(al)}, {vr(al)}")
         b.emit(f"v_mov_b32 {vr(VM[qb])}, {vr(x)}")
-        b.emit(f"v_mul_f32 {vr(VL[qb])}, {vr(VL[qb])}, {vr(al)}")
         tmps = [X0 + 4, X0 + 5, X0 + 6, X0 + 7]
-        for i in range(64):
-            acc = 64 * qb + i
+        for i, acc in enumerate(list(range(64 * qb, 64 * qb + 64)) + list(range(LS + 16 * qb, LS + 16 * qb + 16))):
             t = tmps[i % 4]
             b.emit(f"v_accvgpr_read_b32 {vr(t)}, {ar(acc)}")
             b.emit(f"v_mul_f32 {vr(t)}, {vr(t)}, {vr(al)}")
@@ -300,72 +337,53 @@ def tile_of(b: Block, dst: int, idx_reg: str):
     b.emit(f"s_cselect_b32 {sr(dst)}, {idx_reg}, {sr(S_TMP)}")
 
 
-def dma(b: Block, kt_reg: int, is_k: bool, lds_byte: int, dpw: int):
-    """LDS-direct loads of one 64-key tile (this wave's rows) to LDS byte offset lds_byte."""
+def dma_setup(b: Block, vis_add: int, is_k: bool, rsrc: int):
+    """Buffer descriptor of visit S_T + vis_add: K or V rows of its key tile up
+    to the request end; a zero range when the visit does not exist (the loads
+    then touch no memory and write nothing)."""
     base_lo, base_hi = ("%[kb_lo]", "%[kb_hi]") if is_k else ("%[vb_lo]", "%[vb_hi]")
-    b.emit(f"s_mul_i32 {sr(S_OFF)}, {sr(kt_reg)}, %[rb64]")
-    b.emit(f"s_add_u32 {sr(S_RSRC)}, {base_lo}, {sr(S_OFF)}")
-    b.emit(f"s_addc_u32 {sr(S_RSRC + 1)}, {base_hi}, 0")
-    b.emit(f"s_sub_u32 {sr(S_RSRC + 2)}, %[nrec], {sr(S_OFF)}")
-    b.emit(f"s_mov_b32 {sr(S_RSRC + 3)}, 0x20000")
-    b.emit(f"s_mov_b32 {sr(S_SO)}, %[wsoff]")
-    for i in range(dpw):
-        b.emit(f"s_add_u32 m0, %[wlds], {lds_byte + 1024 * i}")
-        if i:
-            b.emit(f"s_add_u32 {sr(S_SO)}, {sr(S_SO)}, %[rb4]")
-        else:
-            b.emit("s_nop 0")
-        voff = f"%[ko{i % 4}]" if is_k else "%[vo]"
-        b.emit(f"buffer_load_dwordx4 {voff}, {sr(S_RSRC, 4)}, {sr(S_SO)} offen lds")
-
-
-def dma_if(b: Block, vis_add: int, is_k: bool, lds_byte: int, dpw: int, lab: str, count: bool):
-    """Loads of visit S_T + vis_add (when it exists); adds dpw to S_NL when `count`."""
     b.emit(f"s_add_u32 {sr(S_NV1)}, {sr(S_T)}, {vis_add}")
-    b.emit(f"s_cmp_lt_u32 {sr(S_NV1)}, %[nvis]")
-    b.emit(f"s_cbranch_scc0 {lab}")
     tile_of(b, S_LAST, sr(S_NV1))
-    dma(b, S_LAST, is_k, lds_byte, dpw)
-    if count:
-        b.emit(f"s_add_u32 {sr(S_NL)}, {sr(S_NL)}, {dpw}")
-    b.emit(f"{lab}:")
+    b.emit(f"s_mul_i32 {sr(S_OFF)}, {sr(S_LAST)}, %[rb64]")
+    b.emit(f"s_add_u32 {sr(rsrc)}, {base_lo}, {sr(S_OFF)}")
+    b.emit(f"s_addc_u32 {sr(rsrc + 1)}, {base_hi}, 0")
+    b.emit(f"s_sub_u32 {sr(rsrc + 2)}, %[nrec], {sr(S_OFF)}")
+    b.emit(f"s_cmp_lt_u32 {sr(S_NV1)}, %[nvis]")
+    b.emit(f"s_cselect_b32 {sr(rsrc + 2)}, {sr(rsrc + 2)}, 0")
+    b.emit(f"s_mov_b32 {sr(rsrc + 3)}, 0x20000")
 
 
-def wait_loads(b: Block, dpw: int, stages: int, lab: str):
-    """Wait for every load but those issued at the previous barrier (S_NL of them)."""
-    if stages == 2:
-        b.emit("s_waitcnt vmcnt(0)")
-        return
-    b.emit(f"s_cmp_eq_u32 {sr(S_NL)}, {2 * dpw}")
-    b.emit(f"s_cbranch_scc1 {lab}_w2")
-    b.emit(f"s_cmp_eq_u32 {sr(S_NL)}, {dpw}")
-    b.emit(f"s_cbranch_scc1 {lab}_w1")
-    b.emit("s_waitcnt vmcnt(0)")
-    b.emit(f"s_branch {lab}_wd")
-    b.emit(f"{lab}_w1:")
-    b.emit(f"s_waitcnt vmcnt({dpw})")
-    b.emit(f"s_branch {lab}_wd")
-    b.emit(f"{lab}_w2:")
-    b.emit(f"s_waitcnt vmcnt({2 * dpw})")
-    b.emit(f"{lab}_wd:")
+def dma_groups(is_k: bool, rsrc: int, so: int, lds_byte: int, dpw: int) -> list[list[str]]:
+    """The LDS-direct loads of one tile (this wave's rows), one group per load."""
+    groups = []
+    for i in range(dpw):
+        g = [f"s_add_u32 m0, %[wlds], {lds_byte + 1024 * i}"]
+        g.append(f"s_add_u32 {sr(so)}, {sr(so)}, %[rb4]" if i else f"s_mov_b32 {sr(so)}, %[wsoff]")
+        voff = f"%[ko{i % 4}]" if is_k else "%[vo]"
+        g.append(f"buffer_load_dwordx4 {voff}, {sr(rsrc, 4)}, {sr(so)} offen lds")
+        groups.append(g)
+    return groups
 
 
-def barrier_dma(b: Block, tp: int, dpw: int, stages: int, lab: str):
+def barrier_dma(b: Block, tp: int, dpw: int, stages: int) -> list[list[str]]:
     """At tile t' = S_T + tp: wait for the loads tile t' still needs, barrier
-    (every wave is done with K(t') and V(t'-1)), then load K(t' + STAGES) into
-    K stage tp and V(t' + STAGES - 1) into V stage tp - 1."""
-    wait_loads(b, dpw, stages, lab)
+    (every wave is done with K(t') and V(t'-1)), then set up the loads of
+    K(t' + STAGES) into K stage tp and V(t' + STAGES - 1) into V stage tp - 1.
+    Every barrier issues the same 2 dpw loads, so the loads still allowed in
+    flight (those of the previous barrier, with three stages) are a constant."""
+    b.emit(f"s_waitcnt vmcnt({2 * dpw * (stages - 2)})")
     b.emit("s_barrier")
-    b.emit(f"s_mov_b32 {sr(S_NL)}, 0")
-    dma_if(b, tp + stages, True, k_off(tp), dpw, f"{lab}_nok", True)
-    dma_if(b, tp + stages - 1, False, v_lds((tp - 1) % stages, stages), dpw, f"{lab}_nov", True)
+    dma_setup(b, tp + stages, True, S_RSRC)
+    dma_setup(b, tp + stages - 1, False, S_VRSRC)
+    return (dma_groups(True, S_RSRC, S_SO, k_off(tp), dpw) +
+            dma_groups(False, S_VRSRC, S_VSO, v_lds((tp - 1) % stages, stages), dpw))
 
 
 def pv_tail(b: Block, p_prev: int, voff: int):
     b.reset_ds()
     for f in range(8):
         ks, db = divmod(f, 4)
-        buf = VB[f % 3]
+        buf = VB[f % RING]
         off = voff + 4096 * ks
         b.ds_op(f"v{f}", f"ds_read_b64_tr_b16 {vr(buf, 2)}, %[va{db}] offset:{off}")
         b.ds_op(f"v{f}", f"ds_read_b64_tr_b16 {vr(buf + 2, 2)}, %[va{db}] offset:{off + 2048}")
@@ -375,13 +393,17 @@ def pv_tail(b: Block, p_prev: int, voff: int):
             b.wait_ds(f"v{g}")
             for qb in range(2):
                 o = ar(16 * (4 * qb + gdb), 16)
-                b.emit(f"{MFMA} {o}, {vr(VB[g % 3], 4)}, {vr(p_prev + 8 * qb + 4 * gks, 4)}, {o}")
+                b.emit(f"{MFMA} {o}, {vr(VB[g % RING], 4)}, {vr(p_prev + 8 * qb + 4 * gks, 4)}, {o}")
     for g in (6, 7):
         gks, gdb = divmod(g, 4)
         b.wait_ds(f"v{g}")
         for qb in range(2):
             o = ar(16 * (4 * qb + gdb), 16)
-            b.emit(f"{MFMA} {o}, {vr(VB[g % 3], 4)}, {vr(p_prev + 8 * qb + 4 * gks, 4)}, {o}")
+            b.emit(f"{MFMA} {o}, {vr(VB[g % RING], 4)}, {vr(p_prev + 8 * qb + 4 * gks, 4)}, {o}")
+    for ks in range(2):
+        for q in range(2):
+            ls = ar(LS + 16 * q, 16)
+            b.emit(f"{MFMA} {ls}, {vr(ONES, 4)}, {vr(p_prev + 8 * q + 4 * ks, 4)}, {ls}")
 
 
 def loop_block(dpw: int, stages: int) -> list[str]:
@@ -393,42 +415,52 @@ def loop_block(dpw: int, stages: int) -> list[str]:
         b.emit(f"v_accvgpr_write_b32 {ar(i)}, 0")
     for i in range(16):
         b.emit(f"v_mov_b32 {vr(P_B + i)}, 0")
+    for i in range(32):
+        b.emit(f"v_accvgpr_write_b32 {ar(LS + i)}, 0")
     for qb in range(2):
         b.emit(f"v_mov_b32 {vr(VM[qb])}, 0xf149f2ca")  # -1e30
-        b.emit(f"v_mov_b32 {vr(VL[qb])}, 0")
+    for i in range(4):
+        b.emit(f"v_mov_b32 {vr(ONES + i)}, 0x3f803f80")  # bf16 (1, 1)
     b.emit(f"v_mov_b32 {vr(VNINF)}, 0xff800000")
     b.emit(f"s_mov_b32 {sr(S_LIM)}, 0x4b800000")  # 2^24
     b.emit(f"s_mov_b32 {sr(S_T)}, 0")
-    # ---- prologue: K(0 .. STAGES-1) and V(0 .. STAGES-2), the loads the
-    # barriers of visits -STAGES+1 .. -1 would have issued; then QK(0) -> S_A
-    for v in range(stages):
-        dma_if(b, v, True, k_off(v), dpw, f"L_prok{v}", False)
-    for v in range(stages - 1):
-        dma_if(b, v, False, v_lds(v, stages), dpw, f"L_prov{v}", False)
-    b.emit("s_waitcnt vmcnt(0)")
-    b.emit(f"s_mov_b32 {sr(S_NL)}, 0")
+    # ---- prologue: the loads the barriers of visits -STAGES+1 .. -1 would
+    # have issued, K(0) first: K(0), K(1), V(0), then (three stages) K(2),
+    # V(1). Only K(0) is waited for here (QK(0) -> S_A); the barrier of visit
+    # 0 waits for K(1) and V(0) like any other.
+    order = [(0, True), (1, True), (0, False)] + ([(2, True), (1, False)] if stages == 3 else [])
+    for v, is_k in order:
+        rsrc, so = (S_RSRC, S_SO) if is_k else (S_VRSRC, S_VSO)
+        dma_setup(b, v, is_k, rsrc)
+        lds = k_off(v) if is_k else v_lds(v, stages)
+        for g in dma_groups(is_k, rsrc, so, lds, dpw):
+            for ln in g:
+                b.emit(ln)
+    b.emit(f"s_waitcnt vmcnt({dpw * (len(order) - 1)})")
     b.emit("s_barrier")
     b.reset_ds()
     for ds in range(8):
-        b.ds_op(f"k{ds}", f"ds_read_b128 {vr(KB[ds % 3], 4)}, %[ka{ds}] offset:{k_off(0)}")
+        b.ds_op(f"k{ds}", f"ds_read_b128 {vr(KB[ds % RING], 4)}, %[ka{ds}] offset:{k_off(0)}")
         if ds >= 2:
             g = ds - 2
             b.wait_ds(f"k{g}")
             for qb in range(2):
                 acc = vr(S_A + 16 * qb, 16)
-                b.emit(f"{MFMA} {acc}, {vr(KB[g % 3], 4)}, {ar(128 + 32 * qb + 4 * g, 4)}, "
+                b.emit(f"{MFMA} {acc}, {vr(KB[g % RING], 4)}, {ar(128 + 32 * qb + 4 * g, 4)}, "
                        f"{'0' if g == 0 else acc}")
     for g in (6, 7):
         b.wait_ds(f"k{g}")
         for qb in range(2):
             acc = vr(S_A + 16 * qb, 16)
-            b.emit(f"{MFMA} {acc}, {vr(KB[g % 3], 4)}, {ar(128 + 32 * qb + 4 * g, 4)}, {acc}")
+            b.emit(f"{MFMA} {acc}, {vr(KB[g % RING], 4)}, {ar(128 + 32 * qb + 4 * g, 4)}, {acc}")
     for _ in range(3):
         b.emit("s_nop 7")
     # ---- main loop over groups of STAGES tiles (S_T a multiple of STAGES at the top)
     b.emit("L_loop:")
     pos = 0
     slow = []
+    side = []
+    masks = []
     for tp in range(stages):
         # key tile of visit t + tp, and whether its sub-tiles need the mask
         b.emit(f"s_add_u32 {sr(S_NV1)}, {sr(S_T)}, {tp}")
@@ -444,20 +476,20 @@ def loop_block(dpw: int, stages: int) -> list[str]:
                 voff = v_off(tp)
             b.emit(f"s_add_u32 {sr(S_NV1)}, {sr(S_T)}, {tp}")
             b.emit(f"s_cmp_ge_u32 {sr(S_NV1)}, %[a_full]")
-            b.emit(f"s_cbranch_scc0 L_nomask{pos}")
-            mask_code(b, s_cur, h, f"L_nomask{pos}")
+            b.emit(f"s_cbranch_scc1 L_mask{pos}")
+            b.emit(f"L_nomask{pos}:")
+            masks.append((s_cur, h, pos))
             b.emit("s_waitcnt lgkmcnt(0)")
-            step(b, s_cur, s_next, p_cur, p_prev, koff, voff, c)
-            b.emit(f"v_cmp_lt_f32 vcc, {sr(S_LIM)}, {vr(VT[0])}")
-            b.emit(f"v_cmp_lt_f32 {sr(S_M2, 2)}, {sr(S_LIM)}, {vr(VT[1])}")
+            step(b, s_cur, s_next, p_cur, p_prev, koff, voff, c, side)
+            side = []
+            b.emit(f"v_cmp_lt_f32 vcc, {sr(S_LIM)}, {vr(VMX[0])}")
+            b.emit(f"v_cmp_lt_f32 {sr(S_M2, 2)}, {sr(S_LIM)}, {vr(VMX[1])}")
             b.emit(f"s_or_b64 vcc, vcc, {sr(S_M2, 2)}")
             b.emit(f"s_cbranch_vccnz L_slow{pos}")
             b.emit(f"L_ret{pos}:")
-            b.emit(f"v_add_f32 {vr(VL[0])}, {vr(VL[0])}, {vr(VT[0])}")
-            b.emit(f"v_add_f32 {vr(VL[1])}, {vr(VL[1])}, {vr(VT[1])}")
             slow.append((s_cur, p_cur, f"L_slow{pos}", f"L_ret{pos}"))
             if h == 0:
-                barrier_dma(b, tp, dpw, stages, f"L_bar{pos}")
+                side = barrier_dma(b, tp, dpw, stages)
             pos += 1
         # leave after the last visited tile: its second half still needs PV
         b.emit(f"s_add_u32 {sr(S_NV1)}, {sr(S_T)}, {tp + 1}")
@@ -470,13 +502,19 @@ def loop_block(dpw: int, stages: int) -> list[str]:
         pv_tail(b, P_B, v_off(tp) + HALF)
         b.emit("s_branch L_done")
     b.emit("L_done:")
+    b.emit("s_waitcnt vmcnt(0)")  # no load may still be writing LDS when the waves end
     for _ in range(3):
         b.emit("s_nop 7")
-    b.emit(f"v_mov_b32 %[l0], {vr(VL[0])}")
-    b.emit(f"v_mov_b32 %[l1], {vr(VL[1])}")
+    b.emit(f"v_accvgpr_read_b32 %[l0], {ar(LS)}")
+    b.emit(f"v_accvgpr_read_b32 %[l1], {ar(LS + 16)}")
     b.emit("s_branch L_end")
     for args in slow:
         slow_path(b, *args[:2], c, *args[2:])
+    # masks run out of line, so the common path takes no branch
+    for s_cur, h, mpos in masks:
+        b.emit(f"L_mask{mpos}:")
+        mask_code(b, s_cur, h, f"L_mdone{mpos}")
+        b.emit(f"s_branch L_nomask{mpos}")
     b.emit("L_end:")
     return [ln for ln in b.lines if ln]
 
@@ -484,6 +522,7 @@ def loop_block(dpw: int, stages: int) -> list[str]:
 def clobbers() -> list[str]:
     regs = [f'"v{i}"' for i in range(NUM_V)]
     regs += [f'"s{i}"' for i in SGPRS]
+    regs += [f'"a{i}"' for i in range(LS, LS + 32)]
     regs += ['"vcc"', '"scc"', '"m0"', '"memory"']
     return regs
 

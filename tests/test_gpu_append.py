@@ -16,6 +16,16 @@ from gpu_common import TOL_BF16_ATTN, TOL_F32, build, dev, host, say, segments_o
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True, params=["auto", "pipe", "classic"])
+def attention_kernel(request, monkeypatch):
+    """Both bf16 attention kernels, forced, and the one chosen by shape."""
+    if request.param != "auto":
+        monkeypatch.setenv("MIS_ATTENTION_KERNEL", request.param)
+    else:
+        monkeypatch.delenv("MIS_ATTENTION_KERNEL", raising=False)
+    return request.param
+
+
 def _item_mask(wl):
     so = segments_oracle(wl)
     return so["item_id"] >= 0, so
