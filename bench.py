@@ -59,13 +59,32 @@ def lm_head_cost(wl):
     return flops, nbytes
 
 
-def _sha(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+ATTN_SOURCES = ("attn_bf16.hip", "attn_bf16_pipe.hip", "attn_loop.inc")
 
 
-def read_traffic(workload: str, kernel_src: str):
-    """HBM bytes per launch from a committed counter summary, if it matches the kernel source."""
+def attention_source_sha() -> str:
+    """First 16 hex digits of the SHA-256 of the bf16 attention sources (both kernels)."""
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "item_scoring_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def attention_kernel_name(wl, seg) -> str:
+    """The bf16 attention kernel the library launches for this shape (the
+    same rule as its dispatcher: the 64-rows-per-wave kernel when GQA groups
+    of 4+ give every CU at least 8 four-head workgroups)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    gsz = wl.hq // wl.hkv
+    if gsz % 4 == 0 and seg.struct.num_work * (wl.hq // 4) >= 8 * cus:
+        return "attn_pipe_kernel<4>"
+    return "attn_dma_kernel<2, 2>" if gsz % 2 == 0 else "attn_dma_kernel<2, 1>"
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from a committed counter summary, if it matches the kernel sources."""
     path = os.path.join(PROFILES, f"traffic_attention_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -75,7 +94,7 @@ def read_traffic(workload: str, kernel_src: str):
             if ":" in ln and not ln.startswith("#"):
                 key, val = ln.split(":", 1)
                 vals[key.strip()] = val.strip()
-    if vals.get("source_sha256") != _sha(kernel_src):
+    if vals.get("source_sha256") != attention_source_sha():
         return None
     try:
         return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
@@ -338,8 +357,8 @@ def main(argv=None):
     flops = attention_flops(wl)
     tflops = flops / (t_att * 1e-3) / 1e12
 
-    attn_src = os.path.join(ROOT, "item_scoring_attention_amd", "csrc", "attn_bf16.hip")
-    traffic = read_traffic(wl.name, attn_src)
+    traffic = read_traffic(wl.name)
+    attn_kernel = attention_kernel_name(wl, seg)
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -373,7 +392,7 @@ def main(argv=None):
                     "score": round(t_sco_step, 4)},
         "kernel_ms": {"attention": round(t_att, 4), "score": round(t_sco, 4), "rope": round(t_rope, 4)},
         "roofline": {
-            "kernel": "attn_dma_kernel (MIS prefill attention)",
+            "kernel": f"{attn_kernel} (MIS prefill attention)",
             "bound": "mfma",
             "achieved": round(tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
