@@ -73,14 +73,15 @@ def attention_source_sha() -> str:
 
 def attention_kernel_name(wl, seg) -> str:
     """The bf16 attention kernel the library launches for this shape (the
-    same rule as its dispatcher: the 64-rows-per-wave kernel when GQA groups
-    of 4+ give every CU at least 8 four-head workgroups)."""
+    same rule as its dispatcher: 64 query rows per wave when GQA groups of 4+
+    give every CU at least 8 four-head workgroups, else 32 rows per wave for
+    even group sizes, else the plain loop)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     gsz = wl.hq // wl.hkv
     if gsz % 4 == 0 and seg.struct.num_work * (wl.hq // 4) >= 8 * cus:
-        return "attn_pipe_kernel<4>"
-    return "attn_dma_kernel<2, 2>" if gsz % 2 == 0 else "attn_dma_kernel<2, 1>"
+        return "attn_pipe_kernel<4, 1>"
+    return "attn_pipe_kernel<2, 2>" if gsz % 2 == 0 else "attn_dma_kernel<2, 1>"
 
 
 def read_traffic(workload: str):

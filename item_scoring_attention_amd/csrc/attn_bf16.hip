@@ -445,21 +445,25 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
   const __bf16 *kp = static_cast<const __bf16 *>(k);
   const __bf16 *vp = static_cast<const __bf16 *>(v);
   __bf16 *op = static_cast<__bf16 *>(o);
-  // Long runs of work (GQA groups of 4 or more and at least 8 four-head
-  // workgroups per CU) take the kernel with 64 query rows per wave: one wave
-  // per SIMD, so it cannot hide the fixed cost of starting a query tile
-  // behind another workgroup, but its key-tile loop is faster. Otherwise this
-  // kernel (two waves per SIMD): 2 token blocks x 2 heads of one KV head, or
-  // one head for odd group sizes.
-  // MIS_ATTENTION_KERNEL=pipe or =classic forces one of the two (tests run
-  // every shape through both); the pipelined one needs an even group size.
+  // Three kernels. Long runs of work (GQA groups of 4 or more and at least 8
+  // four-head workgroups per CU) take the pipelined loop with 64 query rows
+  // per wave: one wave per SIMD, so it cannot hide the fixed cost of starting
+  // a query tile behind another workgroup, but its loop is the fastest. Other
+  // even group sizes take the pipelined loop with 32 rows per wave, two waves
+  // per SIMD (2 row blocks x 2 heads per workgroup); odd group sizes this
+  // file's kernel (2 row blocks x 1 head, plain loop, two waves per SIMD).
+  // MIS_ATTENTION_KERNEL=pipe, =pipe32 or =classic forces one (tests run
+  // every shape through each); the pipelined ones need an even group size.
   const char *force = std::getenv("MIS_ATTENTION_KERNEL");
   const bool want_pipe = force && std::strcmp(force, "pipe") == 0;
   const bool want_classic = force && std::strcmp(force, "classic") == 0;
+  const bool want_pipe32 = force && std::strcmp(force, "pipe32") == 0;
   const bool pipe_fits = gsz % 2 == 0;
   const bool pipe_pays = gsz % 4 == 0 && int64_t(seg.num_work) * (hq / 4) >= 8 * int64_t(device_cus());
-  if (pipe_fits && (want_pipe || (pipe_pays && !want_classic)))
+  if (pipe_fits && (want_pipe || (pipe_pays && !want_classic && !want_pipe32)))
     return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, st);
+  if (pipe_fits && !want_classic)
+    return launch_attention_bf16_pipe32(seg, q, k, v, o, hq, hkv, scale, items_only, st);
   if (gsz % 2 == 0) return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
   return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
 }

@@ -83,6 +83,17 @@ struct LoopArgs {
     [rb4] "s"(x.rb4), [nrec] "s"(x.nrec), [wsoff] "s"(x.wsoff), [wlds] "s"(x.wlds), [c] "s"(x.c)                  \
   : MIS_ATTN_LOOP_CLOBBERS
 
+#define MIS_ATTN_LOOP_OPERANDS_QB1                                                                                  \
+  : [o0] "={a[0:31]}"(o0), [o1] "={a[32:63]}"(o1), [l0] "=v"(l0)                                                   \
+  : [q0] "{a[64:95]}"(q0), [ka0] "v"(x.ka[0]), [ka1] "v"(x.ka[1]), [ka2] "v"(x.ka[2]), [ka3] "v"(x.ka[3]),         \
+    [ka4] "v"(x.ka[4]), [ka5] "v"(x.ka[5]), [ka6] "v"(x.ka[6]), [ka7] "v"(x.ka[7]), [va0] "v"(x.va[0]),            \
+    [va1] "v"(x.va[1]), [va2] "v"(x.va[2]), [va3] "v"(x.va[3]), [ko0] "v"(x.ko[0]), [ko1] "v"(x.ko[1]),            \
+    [ko2] "v"(x.ko[2]), [ko3] "v"(x.ko[3]), [vo] "v"(x.vo), [rjt0] "v"(x.rjt[0]), [rjb0] "v"(x.rjb[0]),            \
+    [rlq] "v"(x.rlq), [nvis] "s"(x.nvis), [a_end] "s"(x.a_end), [b_start] "s"(x.b_start), [a_full] "s"(x.a_full), \
+    [kb_lo] "s"(x.kb_lo), [kb_hi] "s"(x.kb_hi), [vb_lo] "s"(x.vb_lo), [vb_hi] "s"(x.vb_hi), [rb64] "s"(x.rb64),    \
+    [rb4] "s"(x.rb4), [nrec] "s"(x.nrec), [wsoff] "s"(x.wsoff), [wlds] "s"(x.wlds), [c] "s"(x.c)                  \
+  : MIS_ATTN_LOOP_CLOBBERS_QB1
+
 // Runs the whole key-tile loop; O^T (unnormalised) and the row sums of the
 // lane's two query rows come back. DPW = LDS-direct loads per wave, tile and operand (16 / HP).
 template <int DPW>
@@ -101,21 +112,37 @@ __device__ __forceinline__ void attn_loop(const LoopArgs &x, const f32x32 &q0, c
 #pragma clang diagnostic pop
 }
 
-// K/V stages of the ring: three when one workgroup holds the CU (HP = 4, 96
-// KB of LDS), two when two workgroups share it (HP = 2, 64 KB each).
-template <int HP>
-constexpr int kStages = HP == 4 ? 3 : 2;
+// The same loop for 32 query rows per wave (one query block): four waves
+// load a tile, two K/V stages, and the wave fits in 256 registers.
+__device__ __forceinline__ void attn_loop_qb1(const LoopArgs &x, const f32x32 &q0, f32x32 &o0, f32x32 &o1,
+                                              float &l0) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile(MIS_ATTN_LOOP_TEXT_QB1 MIS_ATTN_LOOP_OPERANDS_QB1);
+#pragma clang diagnostic pop
+}
 
-template <int HP>
-__global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
+// HP heads x TB row blocks per workgroup, one wave each: TB = 1 gives a wave
+// 64 query rows (two 32-row query blocks, one wave per SIMD), TB = 2 gives it
+// 32 rows (two waves per SIMD). K/V stages of the ring: three when one
+// workgroup holds the CU (HP = 4, TB = 1: 96 KB of LDS), two when two
+// workgroups share it (64 KB each).
+template <int HP, int TB>
+constexpr int kStages = HP == 4 && TB == 1 ? 3 : 2;
+
+template <int HP, int TB>
+__global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
     const int32_t *__restrict__ work, const int32_t *__restrict__ cu_seqlens,
     const int32_t *__restrict__ prefix_lens, const int32_t *__restrict__ cu_tiles,
     const int8_t *__restrict__ tile_class, const int32_t *__restrict__ item_id,
     const int32_t *__restrict__ item_begin, const __bf16 *__restrict__ q,
     const __bf16 *__restrict__ k, const __bf16 *__restrict__ v, __bf16 *__restrict__ o, int hq,
     int hkv, float c, int items_only) {
-  constexpr int ROWS_PER_WAVE = BN / HP;  // tile rows each wave loads
-  constexpr int STAGES = kStages<HP>;
+  constexpr int NW = HP * TB;                // waves
+  constexpr int QB = 2 / TB;                 // 32-row query blocks per wave
+  constexpr int ROWS_PER_WAVE = BN / NW;     // tile rows each wave loads
+  constexpr int STAGES = kStages<HP, TB>;
+  static_assert(NW == 2 || NW == 4, "the loop blocks are generated for 8 or 4 loads per wave and tile");
   __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * STAGES * TILE];  // K stages, then V stages
 
   const int gsz = hq / hkv;
@@ -147,18 +174,21 @@ __global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
   const int lane = tid & 63;
   const int g = lane >> 5;
   const int ql = lane & 31;
-  const int head = kvh * gsz + hc * HP + wave;
+  const int hp = wave / TB;
+  const int tb = wave % TB;  // row block: rows 32 tb .. of the query tile (TB = 2)
+  const int head = kvh * gsz + hc * HP + hp;
+  const int row0 = qt * BM + 32 * tb;  // first query row of the wave
 
   const int64_t q_stride = int64_t(hq) * D;
-  // Q^T operands of the two query blocks; rows past the request end read as zeros.
-  f32x32 qv[2];
+  // Q^T operands of the wave's query blocks; rows past the request end read as zeros.
+  f32x32 qv[QB];
   {
     const uint32_t q_bytes = uint32_t(Tr) * uint32_t(q_stride) * 2u - uint32_t(head) * D * 2u;
     const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16 *>(q + int64_t(base) * q_stride + int64_t(head) * D), 0, q_bytes, kRsrcWord3);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const uint32_t qo = uint32_t(qt * BM + 32 * qb + ql) * uint32_t(q_stride) * 2u + 16u * g;
+    for (int qb = 0; qb < QB; ++qb) {
+      const uint32_t qo = uint32_t(row0 + 32 * qb + ql) * uint32_t(q_stride) * 2u + 16u * g;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const f32x4 f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qo + 32u * kk, 0, 0));
@@ -189,11 +219,12 @@ __global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
     x.a_full = __builtin_amdgcn_readfirstlane(first);
   }
 
-  // Mask bounds of the lane's two query rows (j = query block * 32 + lane % 32);
+  // Mask bounds of the lane's query rows (j = row0 + query block * 32 + lane % 32);
   // the lane's keys in a sub-tile are key0 + 8 (a / 4) + a % 4 + 4 g.
+  x.rjt[1] = x.rjb[1] = 0;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int j = qt * BM + 32 * qb + ql;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int j = row0 + 32 * qb + ql;
     const int jb = (j < Tr && j >= lq) ? item_begin[item_id[base + j]] - base : 0;
     x.rjt[qb] = min(j, Tr - 1) - 4 * g;
     x.rjb[qb] = jb - 4 * g;
@@ -205,7 +236,7 @@ __global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
 
   // The V stages start as zeros: rows past the request end are not written
   // by the loads, and the first PV step multiplies a zero P with the last stage.
-  for (int i = tid; i < STAGES * TILE / 8; i += 64 * HP)
+  for (int i = tid; i < STAGES * TILE / 8; i += 64 * NW)
     *reinterpret_cast<uint4 *>(&smem[STAGES * TILE + i * 8]) = make_uint4(0, 0, 0, 0);
 
   const uint32_t lds0 = lds_addr(smem);
@@ -254,17 +285,20 @@ __global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
   __syncthreads();  // V zero fill done before any load lands in LDS
 
   f32x32 o0, o1, o2, o3;
-  float l0, l1;
-  attn_loop<BN / HP / 4>(x, qv[0], qv[1], o0, o1, o2, o3, l0, l1);
+  float l0, l1 = 1.f;
+  if constexpr (QB == 2)
+    attn_loop<BN / HP / 4>(x, qv[0], qv[QB - 1], o0, o1, o2, o3, l0, l1);
+  else
+    attn_loop_qb1(x, qv[0], o0, o1, l0);
 
   // O^T accumulator element a of lane l: dim 8 (a / 4) + 4 g + a % 4 of the
   // 32-dim block, query row l % 32 of the block. l0 and l1 are the full row
-  // sums of the lane's two query rows.
+  // sums of the lane's query rows.
   const float inv0 = 1.0f / l0;
   const float inv1 = 1.0f / l1;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int j = qt * BM + 32 * qb + ql;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int j = row0 + 32 * qb + ql;
     if (j >= Tr) continue;
     const float inv = qb ? inv1 : inv0;
     __bf16 *op = o + int64_t(base + j) * q_stride + int64_t(head) * D;
@@ -283,12 +317,12 @@ __global__ __launch_bounds__(64 * HP, 1) void attn_pipe_kernel(
   }
 }
 
-template <int HP>
+template <int HP, int TB>
 hipError_t launch_pipe(const mis_segments &seg, const void *q, const void *k, const void *v, void *o, int hq,
                        int hkv, float c, int items_only, hipStream_t st) {
   const int64_t blocks = int64_t(seg.num_work) * hq / HP;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  attn_pipe_kernel<HP><<<dim3(unsigned(blocks)), 64 * HP, 0, st>>>(
+  attn_pipe_kernel<HP, TB><<<dim3(unsigned(blocks)), 64 * HP * TB, 0, st>>>(
       seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.item_id, seg.item_begin,
       static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k), static_cast<const __bf16 *>(v),
       static_cast<__bf16 *>(o), hq, hkv, c, items_only);
@@ -304,8 +338,16 @@ hipError_t launch_attention_bf16_pipe(const mis_segments &seg, const void *q, co
   const float c = scale * kLog2e;
   // 4 heads per workgroup share each staged K/V tile among 4 waves (one
   // workgroup per CU, a 3-stage ring); 2 heads run two workgroups per CU.
-  if (gsz % 4 == 0) return launch_pipe<4>(seg, q, k, v, o, hq, hkv, c, items_only, st);
-  return launch_pipe<2>(seg, q, k, v, o, hq, hkv, c, items_only, st);
+  if (gsz % 4 == 0) return launch_pipe<4, 1>(seg, q, k, v, o, hq, hkv, c, items_only, st);
+  return launch_pipe<2, 1>(seg, q, k, v, o, hq, hkv, c, items_only, st);
+}
+
+hipError_t launch_attention_bf16_pipe32(const mis_segments &seg, const void *q, const void *k, const void *v,
+                                        void *o, int hq, int hkv, float scale, int items_only, hipStream_t st) {
+  const int gsz = hq / hkv;
+  if (gsz % 2 != 0) return hipErrorInvalidValue;
+  // 2 heads x 2 row blocks of 32 per workgroup, two workgroups per CU.
+  return launch_pipe<2, 2>(seg, q, k, v, o, hq, hkv, scale * kLog2e, items_only, st);
 }
 
 }  // namespace mis

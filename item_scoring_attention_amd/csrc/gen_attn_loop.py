@@ -61,18 +61,38 @@ def v_off(stage):
 def v_lds(stage, stages):
     return STAGE_BYTES * (stages + stage)
 
-S_A, S_B, P_A, P_B = 0, 32, 64, 80
-RING = 4  # K and V^T fragments in flight (each ring slot is 4 VGPRs)
-KB = tuple(96 + 4 * i for i in range(RING))
-VB = tuple(96 + 4 * RING + 4 * i for i in range(RING))
-E0 = 96 + 8 * RING          # 16 exp temporaries (8 pairs in flight)
-X0 = E0 + 16                # 8 mask / rescale temporaries
-VM = (X0 + 8, X0 + 9)       # running maxima m (exp2 domain)
-VMX = (X0 + 10, X0 + 11)    # largest P of the current sub-tile (overflow check)
-VNINF = X0 + 12             # -inf
-ONES = X0 + 16              # 4 VGPRs of bf16 ones: the A operand of the row-sum MFMAs
-NUM_V = X0 + 20
-LS = 192                    # a[192:223]: row-sum accumulators [qb], 16 AGPRs each
+ILV = False
+
+
+def set_layout(qb: int):
+    """Register map for QB query blocks of 32 rows per wave (2: 64 rows, the
+    map in the module docstring; 1: 32 rows, small enough for two waves per
+    SIMD: S 0-31, P 32-47, 3-deep rings from 48, 8 exp temporaries that the
+    rescale path reuses; O^T a[0:63], Q^T a[64:95], row sums a[96:111])."""
+    global QB, RING, S_A, S_B, P_A, P_B, KB, VB, E0, NPT, X0, VM, VMX, VNINF, ONES, NUM_V, QA, LS
+    QB = qb
+    RING = 4 if qb == 2 else 3         # K and V^T fragments in flight (each ring slot is 4 VGPRs)
+    S_A, S_B = 0, 16 * qb              # S^T of a sub-tile: 16 fp32 per query block
+    P_A, P_B = 32 * qb, 40 * qb        # P^T bf16: 8 dwords per query block
+    r0 = 48 * qb                       # start of the fragment rings
+    KB = tuple(r0 + 4 * i for i in range(RING))
+    VB = tuple(r0 + 4 * RING + 4 * i for i in range(RING))
+    E0 = r0 + 8 * RING                 # exp temporaries: NPT pairs in flight
+    NPT = 8 if qb == 2 else 4
+    # 8 mask / rescale temporaries; with one query block they alias the exp
+    # temporaries (the rescale finishes before its softmax starts)
+    X0 = E0 + 2 * NPT if qb == 2 else E0
+    rest = X0 + 8
+    VM = (rest, rest + 1)              # running maxima m (exp2 domain)
+    VMX = (rest + 2, rest + 3)         # largest P of the current sub-tile (overflow check)
+    VNINF = rest + 4                   # -inf
+    ONES = rest + 8                    # 4 VGPRs of bf16 ones: the A operand of the row-sum MFMAs
+    NUM_V = rest + 12
+    QA = 64 * qb                       # Q^T fragments a[QA:QA + 32 qb]
+    LS = 96 * qb                       # row-sum accumulators [qb], 16 AGPRs each
+
+
+set_layout(2)
 
 # SGPRs used inside the block
 S_T = 40      # visit index of the current tile pair (even)
@@ -145,8 +165,8 @@ def softmax_graph(s_cur: int, p_cur: int, c: str):
     """VALU work turning S_cur into P_cur (bf16) and the largest P per row, as
     (text, cost, deps) nodes. Pair i (qb = i // 8, elements 2pi, 2pi+1):
     two FMAs (c s - m), two exps, a convert into dword pi of P_cur[qb] and a
-    max3 into VMX[qb]. Pair i uses exp temporaries E0 + 2 (i % 8), so pair
-    i + 8 waits for pair i's convert and max (write after read). The row
+    max3 into VMX[qb]. Pair i uses exp temporaries E0 + 2 (i % NPT), so
+    pair i + NPT waits for pair i's convert and max (write after read). The row
     sums are not formed here: 1^T P^T runs on the matrix cores."""
     nodes = []
 
@@ -156,13 +176,13 @@ def softmax_graph(s_cur: int, p_cur: int, c: str):
 
     last_max = {0: None, 1: None}
     done_pair = {}
-    for i in range(16):
+    for i in range(8 * QB):
         qb, pi = divmod(i, 8)
-        ea = E0 + 2 * (i % 8)
+        ea = E0 + 2 * (i % NPT)
         eb = ea + 1
         sa = s_cur + 16 * qb + 2 * pi
         m = VM[qb]
-        war = done_pair.get(i - 8, ())
+        war = done_pair.get(i - NPT, ())
         fa = add(f"v_fma_f32 {vr(ea)}, {vr(sa)}, {c}, -{vr(m)}", 4, war)
         fb = add(f"v_fma_f32 {vr(eb)}, {vr(sa + 1)}, {c}, -{vr(m)}", 4, war)
         xa = add(f"v_exp_f32 {vr(ea)}, {vr(ea)}", 10, [fa])
@@ -217,7 +237,7 @@ def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c, side=()):
     under the matrix pipe."""
     b.reset_ds()
     side = list(side)
-    valu = schedule(softmax_graph(s_cur, p_cur, c), 32, SLOT_BUDGET, HEAD_BUDGET)
+    valu = schedule(softmax_graph(s_cur, p_cur, c), 16 * QB, SLOT_BUDGET, HEAD_BUDGET)
     vi = 0
 
     def k_read(ds):
@@ -242,25 +262,29 @@ def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c, side=()):
     for f in range(RING):
         v_read(f)
     valu_group()
-    for slot in range(32):
-        if slot < 16:
-            ds, qb = divmod(slot, 2)
+    # MFMA order: all QK then all PV, or (ILV) alternating, so that the QK
+    # accumulation chain of a single query block never runs back to back
+    order = ([("qk", i) for i in range(8 * QB)] + [("pv", i) for i in range(8 * QB)] if not ILV else
+             [(kind, i) for i in range(8 * QB) for kind in ("qk", "pv")])
+    for slot, (kind, idx) in enumerate(order):
+        if kind == "qk":
+            ds, qb = divmod(idx, QB)
             b.wait_ds(f"k{ds}")
             acc = vr(s_next + 16 * qb, 16)
             src_c = "0" if ds == 0 else acc
-            b.emit(f"{MFMA} {acc}, {vr(KB[ds % RING], 4)}, {ar(128 + 32 * qb + 4 * ds, 4)}, {src_c}")
-            if qb == 1 and ds + RING < 8:
+            b.emit(f"{MFMA} {acc}, {vr(KB[ds % RING], 4)}, {ar(QA + 32 * qb + 4 * ds, 4)}, {src_c}")
+            if qb == QB - 1 and ds + RING < 8:
                 k_read(ds + RING)
         else:
-            f, qb = divmod(slot - 16, 2)
+            f, qb = divmod(idx, QB)
             ks, db = divmod(f, 4)
             b.wait_ds(f"v{f}")
             o = ar(16 * (4 * qb + db), 16)
             b.emit(f"{MFMA} {o}, {vr(VB[f % RING], 4)}, {vr(p_prev + 8 * qb + 4 * ks, 4)}, {o}")
-            if qb == 1 and f + RING < 8:
+            if qb == QB - 1 and f + RING < 8:
                 v_read(f + RING)
-            if qb == 1 and db == 3:
-                for q in range(2):
+            if qb == QB - 1 and db == 3:
+                for q in range(QB):
                     ls = ar(LS + 16 * q, 16)
                     b.emit(f"{MFMA} {ls}, {vr(ONES, 4)}, {vr(p_prev + 8 * q + 4 * ks, 4)}, {ls}")
         if slot >= 1 and side:
@@ -283,7 +307,7 @@ def mask_code(b: Block, s_cur: int, half: int, skip_label: str):
     for a in range(16):
         ka = 8 * (a // 4) + a % 4
         b.emit(f"s_add_u32 {sr(S_SK)}, {sr(S_KEY0)}, {ka}")
-        for qb in range(2):
+        for qb in range(QB):
             b.emit(f"v_cmp_le_i32 {sr(S_M2, 2)}, {sr(S_SK)}, %[rjt{qb}]")
             b.emit(f"v_cmp_lt_i32 {sr(S_M3, 2)}, {sr(S_SK)}, %[rlq]")
             b.emit(f"v_cmp_ge_i32 vcc, {sr(S_SK)}, %[rjb{qb}]")
@@ -300,7 +324,7 @@ def slow_path(b: Block, s_cur, p_cur, c, label, ret):
     b.emit("s_nop 7")
     b.emit("s_nop 7")
     b.emit("s_nop 7")
-    for qb in range(2):
+    for qb in range(QB):
         s0 = s_cur + 16 * qb
         x, y, z, al = X0, X0 + 1, X0 + 2, X0 + 3
         b.emit(f"v_max3_f32 {vr(x)}, {vr(s0)}, {vr(s0 + 1)}, {vr(s0 + 2)}")
@@ -391,17 +415,17 @@ def pv_tail(b: Block, p_prev: int, voff: int):
             g = f - 2
             gks, gdb = divmod(g, 4)
             b.wait_ds(f"v{g}")
-            for qb in range(2):
+            for qb in range(QB):
                 o = ar(16 * (4 * qb + gdb), 16)
                 b.emit(f"{MFMA} {o}, {vr(VB[g % RING], 4)}, {vr(p_prev + 8 * qb + 4 * gks, 4)}, {o}")
     for g in (6, 7):
         gks, gdb = divmod(g, 4)
         b.wait_ds(f"v{g}")
-        for qb in range(2):
+        for qb in range(QB):
             o = ar(16 * (4 * qb + gdb), 16)
             b.emit(f"{MFMA} {o}, {vr(VB[g % RING], 4)}, {vr(p_prev + 8 * qb + 4 * gks, 4)}, {o}")
     for ks in range(2):
-        for q in range(2):
+        for q in range(QB):
             ls = ar(LS + 16 * q, 16)
             b.emit(f"{MFMA} {ls}, {vr(ONES, 4)}, {vr(p_prev + 8 * q + 4 * ks, 4)}, {ls}")
 
@@ -411,13 +435,13 @@ def loop_block(dpw: int, stages: int) -> list[str]:
     c = "%[c]"
     b.emit("s_waitcnt vmcnt(0) lgkmcnt(0)")
     # ---- init
-    for i in range(128):
+    for i in range(64 * QB):
         b.emit(f"v_accvgpr_write_b32 {ar(i)}, 0")
-    for i in range(16):
+    for i in range(8 * QB):
         b.emit(f"v_mov_b32 {vr(P_B + i)}, 0")
-    for i in range(32):
+    for i in range(16 * QB):
         b.emit(f"v_accvgpr_write_b32 {ar(LS + i)}, 0")
-    for qb in range(2):
+    for qb in range(QB):
         b.emit(f"v_mov_b32 {vr(VM[qb])}, 0xf149f2ca")  # -1e30
     for i in range(4):
         b.emit(f"v_mov_b32 {vr(ONES + i)}, 0x3f803f80")  # bf16 (1, 1)
@@ -444,15 +468,15 @@ def loop_block(dpw: int, stages: int) -> list[str]:
         if ds >= 2:
             g = ds - 2
             b.wait_ds(f"k{g}")
-            for qb in range(2):
+            for qb in range(QB):
                 acc = vr(S_A + 16 * qb, 16)
-                b.emit(f"{MFMA} {acc}, {vr(KB[g % RING], 4)}, {ar(128 + 32 * qb + 4 * g, 4)}, "
+                b.emit(f"{MFMA} {acc}, {vr(KB[g % RING], 4)}, {ar(QA + 32 * qb + 4 * g, 4)}, "
                        f"{'0' if g == 0 else acc}")
     for g in (6, 7):
         b.wait_ds(f"k{g}")
-        for qb in range(2):
+        for qb in range(QB):
             acc = vr(S_A + 16 * qb, 16)
-            b.emit(f"{MFMA} {acc}, {vr(KB[g % RING], 4)}, {ar(128 + 32 * qb + 4 * g, 4)}, {acc}")
+            b.emit(f"{MFMA} {acc}, {vr(KB[g % RING], 4)}, {ar(QA + 32 * qb + 4 * g, 4)}, {acc}")
     for _ in range(3):
         b.emit("s_nop 7")
     # ---- main loop over groups of STAGES tiles (S_T a multiple of STAGES at the top)
@@ -483,8 +507,9 @@ def loop_block(dpw: int, stages: int) -> list[str]:
             step(b, s_cur, s_next, p_cur, p_prev, koff, voff, c, side)
             side = []
             b.emit(f"v_cmp_lt_f32 vcc, {sr(S_LIM)}, {vr(VMX[0])}")
-            b.emit(f"v_cmp_lt_f32 {sr(S_M2, 2)}, {sr(S_LIM)}, {vr(VMX[1])}")
-            b.emit(f"s_or_b64 vcc, vcc, {sr(S_M2, 2)}")
+            if QB == 2:
+                b.emit(f"v_cmp_lt_f32 {sr(S_M2, 2)}, {sr(S_LIM)}, {vr(VMX[1])}")
+                b.emit(f"s_or_b64 vcc, vcc, {sr(S_M2, 2)}")
             b.emit(f"s_cbranch_vccnz L_slow{pos}")
             b.emit(f"L_ret{pos}:")
             slow.append((s_cur, p_cur, f"L_slow{pos}", f"L_ret{pos}"))
@@ -506,7 +531,8 @@ def loop_block(dpw: int, stages: int) -> list[str]:
     for _ in range(3):
         b.emit("s_nop 7")
     b.emit(f"v_accvgpr_read_b32 %[l0], {ar(LS)}")
-    b.emit(f"v_accvgpr_read_b32 %[l1], {ar(LS + 16)}")
+    if QB == 2:
+        b.emit(f"v_accvgpr_read_b32 %[l1], {ar(LS + 16)}")
     b.emit("s_branch L_end")
     for args in slow:
         slow_path(b, *args[:2], c, *args[2:])
@@ -522,7 +548,7 @@ def loop_block(dpw: int, stages: int) -> list[str]:
 def clobbers() -> list[str]:
     regs = [f'"v{i}"' for i in range(NUM_V)]
     regs += [f'"s{i}"' for i in SGPRS]
-    regs += [f'"a{i}"' for i in range(LS, LS + 32)]
+    regs += [f'"a{i}"' for i in range(LS, LS + 16 * QB)]
     regs += ['"vcc"', '"scc"', '"m0"', '"memory"']
     return regs
 
@@ -533,19 +559,28 @@ HEADER = """// Generated by gen_attn_loop.py; do not edit by hand.
 """
 
 
+# (macro suffix, LDS-direct loads per wave and tile, K/V stages, query blocks per wave)
+VARIANTS = (("DPW4", 4, 3, 2), ("DPW8", 8, 2, 2), ("QB1", 4, 2, 1))
+
+
 def render() -> str:
     out = [HEADER]
-    for dpw, stages in ((4, 3), (8, 2)):
+    for name, dpw, stages, qb in VARIANTS:
+        set_layout(qb)
         lines = loop_block(dpw, stages)
         # labels must be unique per asm instance: %= expands to a per-instance number
         text = []
         for ln in lines:
             ln = ln.replace("L_", "L%=_")
             text.append(f'  "{ln}\\n"')
-        out.append(f"#define MIS_ATTN_LOOP_TEXT_DPW{dpw} \\")
+        out.append(f"#define MIS_ATTN_LOOP_TEXT_{name} \\")
         out.append(" \\\n".join(text))
         out.append("")
+    set_layout(2)
     out.append("#define MIS_ATTN_LOOP_CLOBBERS " + ", ".join(clobbers()))
+    set_layout(1)
+    out.append("#define MIS_ATTN_LOOP_CLOBBERS_QB1 " + ", ".join(clobbers()))
+    set_layout(2)
     out.append("")
     return "\n".join(out)
 

@@ -45,6 +45,12 @@ hipError_t launch_attention_bf16_pipe(const mis_segments &seg, const void *q, co
                                       const void *v, void *o, int hq, int hkv, float scale,
                                       int items_only, hipStream_t stream);
 
+// The same loop with 32 query rows per wave, two waves per SIMD (even GQA
+// group sizes, head_dim 128).
+hipError_t launch_attention_bf16_pipe32(const mis_segments &seg, const void *q, const void *k,
+                                        const void *v, void *o, int hq, int hkv, float scale,
+                                        int items_only, hipStream_t stream);
+
 // Inverse frequencies theta^(-2i/D) of the rotary embedding, i < D/2.
 struct RopeFreq {
   double inv[64];

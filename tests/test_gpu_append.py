@@ -16,9 +16,9 @@ from gpu_common import TOL_BF16_ATTN, TOL_F32, build, dev, host, say, segments_o
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(autouse=True, params=["auto", "pipe", "classic"])
+@pytest.fixture(autouse=True, params=["auto", "pipe", "pipe32", "classic"])
 def attention_kernel(request, monkeypatch):
-    """Both bf16 attention kernels, forced, and the one chosen by shape."""
+    """Each bf16 attention kernel, forced, and the one chosen by shape."""
     if request.param != "auto":
         monkeypatch.setenv("MIS_ATTENTION_KERNEL", request.param)
     else:

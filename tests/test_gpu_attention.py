@@ -16,11 +16,12 @@ from gpu_common import (TOL_BF16_ATTN, TOL_F32, attention, build, host, sample_r
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(autouse=True, params=["auto", "pipe", "classic"])
+@pytest.fixture(autouse=True, params=["auto", "pipe", "pipe32", "classic"])
 def attention_kernel(request, monkeypatch):
     """Run every case with the bf16 kernel chosen by shape, and forced to each
-    of the two kernels (64 query rows per wave with the pipelined loop, or two
-    waves per SIMD); the fp32 cases do not depend on it."""
+    of the three kernels (the pipelined loop with 64 or with 32 query rows per
+    wave, or the plain loop with two waves per SIMD); the fp32 cases do not
+    depend on it."""
     if request.param != "auto":
         monkeypatch.setenv("MIS_ATTENTION_KERNEL", request.param)
     else:
