@@ -16,6 +16,9 @@
 // Pass 2 (one wave per item): merge the partials exactly,
 // lse = M + log(sum_c s_c * exp(m_c - M)), and write z_label - lse (or the
 // softmax over the label logits).
+#include <cstdlib>
+#include <cstring>
+
 #include "gfx950_util.h"
 #include "mis_internal.h"
 
@@ -334,6 +337,198 @@ __global__ __launch_bounds__(256) void score_lds_kernel(
   }
 }
 
+// ------------------------------- bf16 LDS-staged, wide tiles (H % 64 == 0)
+// For many items the contraction is MFMA-bound, and with 32 vocabulary rows
+// per wave the fragment reads (one W fragment and NI readout fragments per
+// NI MFMAs, every readout fragment read by all four waves) outrun the LDS.
+// Here a wave owns 64 vocabulary rows, so a readout fragment feeds two MFMAs:
+// workgroup tile 256 rows x 32*NI items, one workgroup per CU, NS-deep ring
+// of 64-dim chunks. Staging, swizzle and the epilogue follow score_lds_kernel.
+template <int NI, int NS>
+__global__ __launch_bounds__(256, 1) void score_wide_kernel(
+    const __bf16 *__restrict__ hidden, const __bf16 *__restrict__ w, int H, int V, int N,
+    const int32_t *__restrict__ readout_pos, LabelArgs labels, float *__restrict__ pmax,
+    float *__restrict__ psum, float *__restrict__ plab, int nvt, int nit) {
+  constexpr int BVW = 256;                     // vocabulary rows of the tile
+  constexpr int NIT = 32 * NI;                 // items in the tile
+  constexpr int WCH = BVW * 64;                // bf16 elements of a staged W chunk
+  constexpr int XCH = NIT * 64;                // ... and of a staged X chunk
+  constexpr int PER_CHUNK = BVW / 32 + NI;     // vector-memory ops per wave per chunk
+  struct Smem {
+    __bf16 w[NS][WCH];
+    __bf16 x[NS][XCH];
+    float red[4][NI][32];
+  };
+  static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) Smem sm;
+  auto &ws_ = sm.w;
+  auto &xs = sm.x;
+  auto &red = sm.red;
+
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int vt = 8 * (jx / nit) + xcd;
+  const int n0 = (jx % nit) * NIT;
+  if (vt >= nvt) return;
+  const int v0 = vt * BVW;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 5, ql = lane & 31;
+  const int piece = lane & 7;
+
+  // W rows v0 .. v0 + 255 (rows past V read as zero). Instruction i of this
+  // wave stages rows 64*wave + 8*i .. +8.
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16 *>(w + int64_t(v0) * H), 0, uint32_t(min(BVW, V - v0)) * uint32_t(H) * 2u,
+      kRsrcWord3);
+  uint32_t woff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 64 * wave + 8 * i + (lane >> 3);
+    woff[i] = uint32_t(r) * uint32_t(H) * 2u + 16u * uint32_t(piece ^ ((r >> 1) & 7));
+  }
+  // Readout rows: instruction i of this wave stages items 32*i + 8*wave .. +8.
+  const __bf16 *xsrc[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int n = 32 * i + 8 * wave + (lane >> 3);
+    xsrc[i] = hidden + int64_t(readout_pos[min(n0 + n, N - 1)]) * H + 8 * (piece ^ ((n >> 1) & 7));
+  }
+
+  f32x16 acc[2][NI];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) acc[mi][ni][a] = 0.f;
+
+  const int nch = H / 64;
+  auto issue = [&](int c, int slot) {
+    const bool real = c < nch;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      lds_load16(wrs, &ws_[slot][(64 * wave + 8 * i) * 64], real ? woff[i] + 128u * uint32_t(c) : 0x80000000u);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) lds_load16(xsrc[i] + (real ? 64 * c : 0), &xs[slot][(32 * i + 8 * wave) * 64]);
+  };
+
+  // LDS read offsets (elements) of this lane's fragments for k-step st.
+  int wrd[2][4], xrd[NI][4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int wr = 64 * wave + 32 * mi + ql;
+      wrd[mi][st] = wr * 64 + 8 * ((4 * g + st) ^ ((wr >> 1) & 7));
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int n = 32 * ni + ql;
+      xrd[ni][st] = n * 64 + 8 * ((4 * g + st) ^ ((n >> 1) & 7));
+    }
+  }
+
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue(p, p);
+  int slot = 0;
+  for (int c = 0; c < nch; ++c) {
+    // chunk c landed: this wave's loads (NS - 2 chunks were issued after
+    // it), then everyone's; the slot chunk c - 1 used is free again.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * PER_CHUNK));
+    barrier_no_fence();
+    const __bf16 *wb = ws_[slot];
+    const __bf16 *xb = xs[slot];
+    bf16x8 af[4][2], bfr[4][NI];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) af[st][mi] = *reinterpret_cast<const bf16x8 *>(wb + wrd[mi][st]);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) bfr[st][ni] = *reinterpret_cast<const bf16x8 *>(xb + xrd[ni][st]);
+    }
+    issue(c + NS - 1, slot == 0 ? NS - 1 : slot - 1);
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[st][mi], bfr[st][ni], acc[mi][ni], 0, 0, 0);
+    // Issue order: the fragments of k-steps 0 and 1, then the MFMAs with the
+    // other fragment reads after the first step's, and the LDS-direct loads
+    // of a later chunk one after each MFMA: a wave issues in order, so a run
+    // of loads would hold the matrix cores back.
+    constexpr int RD = 2 + NI, MF = 2 * NI, LD = PER_CHUNK;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RD, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * MF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < LD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (i == MF - 1 || i == 2 * MF - 1) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+    }
+    slot = slot + 1 == NS ? 0 : slot + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing loads land before the workgroup ends
+
+  // element a of acc[mi][ni] is z[row v0 + 64*wave + 32*mi + 8*(a/4) + 4*g + a%4][item n0 + 32*ni + ql]
+  auto row_of = [&](int mi, int a) { return v0 + 64 * wave + 32 * mi + 8 * (a >> 2) + 4 * g + (a & 3); };
+  float m[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    float x = -INFINITY;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int a = 0; a < 16; ++a)
+        if (row_of(mi, a) < V) x = fmaxf(x, acc[mi][ni][a]);
+    x = fmaxf(x, __shfl_xor(x, 32));
+    if (g == 0) red[wave][ni][ql] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    m[ni] = fmaxf(fmaxf(red[0][ni][ql], red[1][ni][ql]), fmaxf(red[2][ni][ql], red[3][ni][ql]));
+  __syncthreads();
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    float sum = 0.f;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int a = 0; a < 16; ++a)
+        if (row_of(mi, a) < V) sum += fast_exp(acc[mi][ni][a] - m[ni]);
+    sum += __shfl_xor(sum, 32);
+    if (g == 0) red[wave][ni][ql] = sum;
+  }
+  __syncthreads();
+  if (wave == 0 && g == 0) {
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int n = n0 + 32 * ni + ql;
+      if (n < N) {
+        pmax[int64_t(vt) * N + n] = m[ni];
+        psum[int64_t(vt) * N + n] = red[0][ni][ql] + red[1][ni][ql] + red[2][ni][ql] + red[3][ni][ql];
+      }
+    }
+  }
+  for (int kx = 0; kx < labels.k; ++kx) {
+    const int ro = labels.ids[kx] - v0 - 64 * wave;
+    if (ro < 0 || ro >= 64) continue;
+    const int mi = ro >> 5, rr = ro & 31;
+    if (((rr >> 2) & 1) != g) continue;
+    const int at = 4 * (rr >> 3) + (rr & 3);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      float z = 0.f;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) z = (a == at) ? (mi ? acc[1][ni][a] : acc[0][ni][a]) : z;
+      const int n = n0 + 32 * ni + ql;
+      if (n < N) plab[int64_t(n) * labels.k + kx] = z;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32
 // One workgroup per (128 vocabulary rows, item); one thread per row.
 __global__ __launch_bounds__(BV) void score_f32_kernel(
@@ -429,6 +624,7 @@ hipError_t launch_score(const int32_t *readout_pos, int N, const void *hidden, i
                         int V, mis_dtype dt, const LabelArgs &labels, int apply_softmax,
                         float *scores, float *ws, hipStream_t st) {
   const int nvt = score_vocab_tiles(V);
+  int nvt_used = nvt;  // vocabulary tiles of the kernel that runs (the workspace fits the most)
   const size_t part = ((sizeof(float) * size_t(N) * nvt + 255) / 256) * 256;
   float *pmax = ws;
   float *psum = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + part);
@@ -436,7 +632,38 @@ hipError_t launch_score(const int32_t *readout_pos, int N, const void *hidden, i
   if (dt == MIS_BF16) {
     const __bf16 *hp = static_cast<const __bf16 *>(hidden);
     const __bf16 *wp = static_cast<const __bf16 *>(lm_head);
-    if (H % 64 == 0) {
+    // MIS_SCORE_KERNEL=narrow or =wide (=wideNI: NI item blocks) forces a kernel
+    // (tests run every shape through both); otherwise up to 64 items stream W
+    // through the narrow tiles and more items take the wide ones.
+    const char *force = std::getenv("MIS_SCORE_KERNEL");
+    const bool want_narrow = force && std::strncmp(force, "narrow", 6) == 0;
+    const bool want_wide = force && std::strncmp(force, "wide", 4) == 0;
+    if (H % 64 == 0 && !want_narrow && (want_wide || N > 64)) {
+      // item blocks per tile: the fewest padded items, then the widest tile
+      int ni = want_wide && force[4] ? std::atoi(force + 4) : 0;
+      if (ni != 3 && ni != 4 && ni != 5 && ni != 6 && ni != 8) {
+        ni = 3;
+        for (int c : {4, 5, 6, 8}) {
+          const int pc = (N + 32 * c - 1) / (32 * c) * 32 * c, pb = (N + 32 * ni - 1) / (32 * ni) * 32 * ni;
+          if (pc <= pb) ni = c;
+        }
+      }
+      const int nvw = (V + 255) / 256;
+      const int nit = (N + 32 * ni - 1) / (32 * ni);
+      const unsigned grid = unsigned((nvw + 7) / 8 * 8 * nit);
+#define MIS_WIDE(NI, NS)                                                                                  \
+  score_wide_kernel<NI, NS><<<grid, 256, 0, st>>>(hp, wp, H, V, N, readout_pos, labels, pmax, psum, plab, \
+                                                  nvw, nit)
+      switch (ni) {
+        case 3: MIS_WIDE(3, 3); break;
+        case 4: MIS_WIDE(4, 3); break;
+        case 5: MIS_WIDE(5, 3); break;
+        case 6: MIS_WIDE(6, 2); break;
+        default: MIS_WIDE(8, 2); break;
+      }
+#undef MIS_WIDE
+      nvt_used = nvw;
+    } else if (H % 64 == 0) {
       // 32, 64 or 128 items per workgroup; a 3-deep ring while W is streamed
       // once (N <= 64), 2-deep (2 workgroups per CU) when item tiles reuse it
       const int ni = N <= 32 ? 1 : N <= 64 ? 2 : 4;
@@ -468,7 +695,7 @@ hipError_t launch_score(const int32_t *readout_pos, int N, const void *hidden, i
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_kernel<<<N, 256, 0, st>>>(pmax, psum, plab, nvt, N, labels.k, apply_softmax, scores);
+  combine_kernel<<<N, 256, 0, st>>>(pmax, psum, plab, nvt_used, N, labels.k, apply_softmax, scores);
   return hipGetLastError();
 }
 

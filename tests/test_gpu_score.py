@@ -16,6 +16,18 @@ from gpu_common import (TOL_BF16_SCORE, TOL_F32, build, dev, hidden_with_sentine
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True, params=["auto", "narrow", "wide4", "wide6"])
+def score_kernel(request, monkeypatch):
+    """Every case with the bf16 LM-head kernel chosen by shape (narrow tiles up
+    to 64 items, else wide tiles with 3, 5 or 8 item blocks), and forced to the
+    narrow tiles and to wide tiles of 4 and 6 item blocks."""
+    if request.param != "auto":
+        monkeypatch.setenv("MIS_SCORE_KERNEL", request.param)
+    else:
+        monkeypatch.delenv("MIS_SCORE_KERNEL", raising=False)
+    return request.param
+
+
 def _score(wl, seg, hid, W, labels, apply_softmax=False):
     s = mis.mis_score_labels(seg, dev(hid), dev(W), labels, apply_softmax=apply_softmax)
     torch.cuda.synchronize()
