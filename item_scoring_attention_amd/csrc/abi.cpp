@@ -73,9 +73,13 @@ class StageRing {
       if (e != hipSuccess) return e;
     }
     if (s.cap < bytes) {
-      if (s.host) hipHostFree(s.host);
+      void *old = s.host;
       s.host = nullptr;
       s.cap = 0;
+      if (old) {
+        e = hipHostFree(old);
+        if (e != hipSuccess) return e;
+      }
       const size_t cap = std::max<size_t>(bytes, 64 * 1024);
       e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
       if (e != hipSuccess) return e;

@@ -232,8 +232,10 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&sacc)[2], float c, f
     }
 }
 
+// Two workgroups per CU (the 64 KB of K/V stages allow no more): two waves
+// per SIMD with 2 heads, one with a single head.
 template <int TB, int HP>
-__global__ __launch_bounds__(64 * TB * HP, 2) void attn_dma_kernel(
+__global__ __launch_bounds__(64 * TB * HP, HP == 2 ? 2 : 1) void attn_dma_kernel(
     const int32_t *__restrict__ work, const int32_t *__restrict__ cu_seqlens,
     const int32_t *__restrict__ prefix_lens, const int32_t *__restrict__ cu_tiles,
     const int8_t *__restrict__ tile_class, const int32_t *__restrict__ item_id,

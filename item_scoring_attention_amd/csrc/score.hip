@@ -74,7 +74,6 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(
 #pragma unroll
       for (int a = 0; a < 16; ++a) acc[mi][ni][a] = 0.f;
 
-#pragma unroll 2
   for (int h = 0; h < H; h += 32) {
     bf16x8 af[2][2], bf[NI][2];
 #pragma unroll

@@ -100,6 +100,26 @@ def test_item_and_vocab_edges(dtype, n_items, vocab):
         assert np.abs(got).max() <= tol  # a one-word vocabulary has log-prob 0
 
 
+@pytest.mark.parametrize("hidden", [32, 96, 160])
+@pytest.mark.parametrize("n_items,vocab", [(5, 1000), (70, 129), (200, 300)])
+def test_hidden_not_a_multiple_of_64(hidden, n_items, vocab):
+    # bf16 scoring with H % 64 != 0 takes the kernel that reads both operands
+    # from global memory (one, two or four item blocks by N)
+    wl = workloads.from_lengths("h32", [10], [[2] * n_items], hq=4, hkv=2, d=128, hidden=hidden,
+                                vocab=vocab, num_labels=2)
+    so = segments_oracle(wl)
+    seg = build(wl)
+    hid = hidden_with_sentinels(wl, so["readout_pos"])
+    W = workloads.lm_head(wl)
+    labels = sorted({0, vocab - 1, vocab // 3})
+    got = _score(wl, seg, hid, W, labels)
+    ref = oracle.label_scores(hid, so["readout_pos"], W, labels)
+    assert np.abs(got - ref).max() <= TOL_BF16_SCORE
+    p = _score(wl, seg, hid, W, labels, apply_softmax=True)
+    refp = oracle.label_scores(hid, so["readout_pos"], W, labels, apply_softmax=True)
+    assert np.abs(p - refp).max() <= TOL_BF16_SCORE
+
+
 def test_duplicate_labels_repeat_columns():
     wl = workloads.from_lengths("dup", [20], [[4] * 5], hq=4, hkv=2, d=128, hidden=128, vocab=5000,
                                 num_labels=2)
