@@ -318,8 +318,12 @@ def mask_code(b: Block, s_cur: int, half: int, skip_label: str):
     b.emit(f"{skip_label}:")
 
 
-def slow_path(b: Block, s_cur, p_cur, c, label, ret):
-    """Raise m to the sub-tile maximum, rescale O and the row sums, recompute P."""
+def slow_path(b: Block, s_cur, p_cur, c, label, ret, first=False):
+    """Raise m to the sub-tile maximum, rescale O and the row sums, recompute P.
+
+    `first`: this step can hold the query tile's first sub-tile (visit 0's
+    first half). There O and the row sums are still zero (the PV and row-sum
+    MFMAs so far multiplied zero P), so on visit 0 the rescale is skipped."""
     b.emit(f"{label}:")
     b.emit("s_nop 7")
     b.emit("s_nop 7")
@@ -342,12 +346,17 @@ def slow_path(b: Block, s_cur, p_cur, c, label, ret):
         b.emit(f"v_sub_f32 {vr(al)}, {vr(VM[qb])}, {vr(x)}")
         b.emit(f"v_exp_f32 {vr(al)}, {vr(al)}")
         b.emit(f"v_mov_b32 {vr(VM[qb])}, {vr(x)}")
+        if first:
+            b.emit(f"s_cmp_eq_u32 {sr(S_T)}, 0")
+            b.emit(f"s_cbranch_scc1 {label}_nr{qb}")
         tmps = [X0 + 4, X0 + 5, X0 + 6, X0 + 7]
         for i, acc in enumerate(list(range(64 * qb, 64 * qb + 64)) + list(range(LS + 16 * qb, LS + 16 * qb + 16))):
             t = tmps[i % 4]
             b.emit(f"v_accvgpr_read_b32 {vr(t)}, {ar(acc)}")
             b.emit(f"v_mul_f32 {vr(t)}, {vr(t)}, {vr(al)}")
             b.emit(f"v_accvgpr_write_b32 {ar(acc)}, {vr(t)}")
+        if first:
+            b.emit(f"{label}_nr{qb}:")
     for ln in softmax_ops(s_cur, p_cur, c):
         b.emit(ln)
     b.emit(f"s_branch {ret}")
@@ -534,8 +543,8 @@ def loop_block(dpw: int, stages: int) -> list[str]:
     if QB == 2:
         b.emit(f"v_accvgpr_read_b32 %[l1], {ar(LS + 16)}")
     b.emit("s_branch L_end")
-    for args in slow:
-        slow_path(b, *args[:2], c, *args[2:])
+    for i, args in enumerate(slow):
+        slow_path(b, *args[:2], c, *args[2:], first=(i == 0))
     # masks run out of line, so the common path takes no branch
     for s_cur, h, mpos in masks:
         b.emit(f"L_mask{mpos}:")
