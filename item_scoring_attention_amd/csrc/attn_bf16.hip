@@ -238,8 +238,7 @@ template <int TB, int HP>
 __global__ __launch_bounds__(64 * TB * HP, HP == 2 ? 2 : 1) void attn_dma_kernel(
     const int32_t *__restrict__ work, const int32_t *__restrict__ cu_seqlens,
     const int32_t *__restrict__ prefix_lens, const int32_t *__restrict__ cu_tiles,
-    const int8_t *__restrict__ tile_class, const int32_t *__restrict__ item_id,
-    const int32_t *__restrict__ item_begin, const __bf16 *__restrict__ q,
+    const int8_t *__restrict__ tile_class, const int32_t *__restrict__ pos_id, const __bf16 *__restrict__ q,
     const __bf16 *__restrict__ k, const __bf16 *__restrict__ v, __bf16 *__restrict__ o, int hq,
     int hkv, float c /* softmax scale * log2(e) */, int items_only) {
   constexpr int NW = TB * HP;             // waves
@@ -285,7 +284,9 @@ __global__ __launch_bounds__(64 * TB * HP, HP == 2 ? 2 : 1) void attn_dma_kernel
   const int head = kvh * gsz + hc * HP + hp;
   const int j = qt * BMT + tb * 32 + ql;
   const bool row_ok = j < Tr;
-  const int jb = (row_ok && j >= lq) ? item_begin[item_id[base + j]] - base : 0;
+  // an item row at offset d of its item has position id lq + d (the reused
+  // positions), so its item starts at row j - d
+  const int jb = (row_ok && j >= lq) ? j - (pos_id[base + j] - lq) : 0;
 
   const int64_t q_stride = int64_t(hq) * D;
   const int64_t kv_stride = int64_t(hkv) * D;
@@ -430,8 +431,8 @@ hipError_t launch_variant(const mis_segments &seg, const __bf16 *qp, const __bf1
   const int64_t blocks = int64_t(seg.num_work) * hq / HP;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   attn_dma_kernel<TB, HP><<<dim3(unsigned(blocks)), 64 * TB * HP, 0, st>>>(
-      seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.item_id,
-      seg.item_begin, qp, kp, vp, op, hq, hkv, c, items_only);
+      seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.pos_id, qp, kp, vp, op,
+      hq, hkv, c, items_only);
   return hipGetLastError();
 }
 

@@ -1,4 +1,6 @@
-// bf16 MIS prefill attention on CDNA4 MFMA (gfx950), 64 query rows per wave.
+// bf16 MIS prefill attention on CDNA4 MFMA (gfx950) with a software-pipelined
+// key-tile loop: 64 query rows per wave (attn_pipe_kernel<HP, 1>) or 32 rows
+// per wave and two waves per SIMD (attn_pipe_kernel<2, 2>).
 //
 // Computes O = softmax(scale * Q K^T + M) V per query head with the mask M of
 // From Generation to Scoring, §4.1, Eq. 4 (a prefix row sees the prefix up to
@@ -12,11 +14,14 @@
 // transposing V^T reads alone (ds_read_b64_tr_b16 moves half the bytes of a
 // ds_read_b128 per instruction) cap the PV product below the MFMA rate. The
 // price is registers: O^T (128) and Q^T (64) live in AGPRs, S, P and the
-// fragment rings in VGPRs, one wave per SIMD.
+// fragment rings in VGPRs, one wave per SIMD. The 32-row loop fits two waves
+// per SIMD, so one workgroup's start and finish overlap another's loop.
 //
 // Work decomposition: a workgroup takes one 64-token query tile, one KV head
-// and HP of its query heads (one wave per head), and stages each 64-key K and
-// V tile once for all HP waves. HP = 4 runs one workgroup per CU, HP = 2 two.
+// and HP of its query heads; with TB = 1 one wave per head owns the 64 rows,
+// with TB = 2 two waves per head own 32 rows each. It stages each 64-key K
+// and V tile once for all its waves. <4, 1> runs one workgroup per CU, <2, 1>
+// and <2, 2> two.
 // The KV head varies fastest over blockIdx, so with 8 KV heads each XCD (the
 // dispatcher deals workgroups round-robin to the 8 XCDs) serves one KV head
 // from its own L2. Query tiles arrive longest first (the builder's work list).
@@ -27,8 +32,9 @@
 // moves the accumulators between the two files on every step.
 //
 // Layouts (shared with the LDS-direct loads the block issues):
-//   LDS: the K stages, then the V stages, 16 KB each, 64 keys x 256-byte rows; chunk c (16 bytes) of K row r sits in slot c ^ (r & 15),
-//   of V row r in slot c ^ 4 (r & 3), so the K reads (ds_read_b128, 16
+//   LDS: the K stages, then the V stages, 16 KB each, 64 keys x 256-byte
+//   rows; chunk c (16 bytes) of K row r sits in slot c ^ (r & 15), of V row
+//   r in slot c ^ 4 (r & 3), so the K reads (ds_read_b128, 16
 //   consecutive keys at one chunk) and the transposing V reads are free of
 //   bank conflicts.
 //   MFMA v_mfma_f32_32x32x16_bf16: S^T = K Q^T with the keys on the rows, so a
@@ -134,8 +140,7 @@ template <int HP, int TB>
 __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
     const int32_t *__restrict__ work, const int32_t *__restrict__ cu_seqlens,
     const int32_t *__restrict__ prefix_lens, const int32_t *__restrict__ cu_tiles,
-    const int8_t *__restrict__ tile_class, const int32_t *__restrict__ item_id,
-    const int32_t *__restrict__ item_begin, const __bf16 *__restrict__ q,
+    const int8_t *__restrict__ tile_class, const int32_t *__restrict__ pos_id, const __bf16 *__restrict__ q,
     const __bf16 *__restrict__ k, const __bf16 *__restrict__ v, __bf16 *__restrict__ o, int hq,
     int hkv, float c, int items_only) {
   constexpr int NW = HP * TB;                // waves
@@ -225,7 +230,9 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int j = row0 + 32 * qb + ql;
-    const int jb = (j < Tr && j >= lq) ? item_begin[item_id[base + j]] - base : 0;
+    // an item row at offset d of its item has position id lq + d (the
+    // reused positions), so its item starts at row j - d
+    const int jb = (j < Tr && j >= lq) ? j - (pos_id[base + j] - lq) : 0;
     x.rjt[qb] = min(j, Tr - 1) - 4 * g;
     x.rjb[qb] = jb - 4 * g;
   }
@@ -323,7 +330,7 @@ hipError_t launch_pipe(const mis_segments &seg, const void *q, const void *k, co
   const int64_t blocks = int64_t(seg.num_work) * hq / HP;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   attn_pipe_kernel<HP, TB><<<dim3(unsigned(blocks)), 64 * HP * TB, 0, st>>>(
-      seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.item_id, seg.item_begin,
+      seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.pos_id,
       static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k), static_cast<const __bf16 *>(v),
       static_cast<__bf16 *>(o), hq, hkv, c, items_only);
   return hipGetLastError();
