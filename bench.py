@@ -74,12 +74,14 @@ def attention_source_sha() -> str:
 def attention_kernel_name(wl, seg) -> str:
     """The bf16 attention kernel the library launches for this shape (the
     same rule as its dispatcher: 64 query rows per wave when GQA groups of 4+
-    give every CU at least 8 four-head workgroups, else 32 rows per wave for
-    even group sizes, else the plain loop)."""
+    with query tiles of 48+ visited key tiles on average give every CU at
+    least 8 four-head workgroups, else 32 rows per wave for even group sizes,
+    else the plain loop)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     gsz = wl.hq // wl.hkv
-    if gsz % 4 == 0 and seg.struct.num_work * (wl.hq // 4) >= 8 * cus:
+    st = seg.struct
+    if gsz % 4 == 0 and st.num_visits >= 48 * st.num_work and st.num_work * (wl.hq // 4) >= 8 * cus:
         return "attn_pipe_kernel<4, 1>"
     return "attn_pipe_kernel<2, 2>" if gsz % 2 == 0 else "attn_dma_kernel<2, 1>"
 

@@ -81,6 +81,7 @@ typedef struct mis_segments {
   int32_t num_tiles;    /* sum over requests of ceil(T_r/bm) * ceil(T_r/bn) */
   int32_t num_work;     /* sum over requests of ceil(T_r/bm): query tiles */
   int32_t max_seqlen;   /* max_r T_r */
+  int32_t num_visits;   /* sum over the work list of visited key tiles (the tiles with a visible cell) */
   /* per request */
   const int32_t *cu_seqlens;  /* [B+1] packed token offsets */
   const int32_t *prefix_lens; /* [B]   Lq of each request */

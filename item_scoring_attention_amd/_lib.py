@@ -54,6 +54,7 @@ class MisSegments(ctypes.Structure):
         ("num_tiles", ctypes.c_int32),
         ("num_work", ctypes.c_int32),
         ("max_seqlen", ctypes.c_int32),
+        ("num_visits", ctypes.c_int32),
         ("cu_seqlens", ctypes.c_void_p),
         ("prefix_lens", ctypes.c_void_p),
         ("cu_items", ctypes.c_void_p),

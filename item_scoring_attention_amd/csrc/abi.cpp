@@ -290,6 +290,8 @@ int mis_build_segments(int32_t B, const int32_t *cu_seqlens_h, const int32_t *pr
     }
   }
   std::stable_sort(wl.begin(), wl.end(), [](const Work &x, const Work &y) { return x.cost > y.cost; });
+  int64_t visits = 0;
+  for (const Work &x : wl) visits += x.cost;
   int32_t *wdst = reinterpret_cast<int32_t *>(img.data() + L.work);
   for (size_t i = 0; i < wl.size(); ++i) {
     wdst[4 * i + 0] = wl[i].r;
@@ -308,6 +310,7 @@ int mis_build_segments(int32_t B, const int32_t *cu_seqlens_h, const int32_t *pr
   s.num_tiles = int32_t(tiles);
   s.num_work = int32_t(work);
   s.max_seqlen = max_len;
+  s.num_visits = int32_t(visits);  // at most num_tiles
   s.cu_seqlens = reinterpret_cast<const int32_t *>(base + L.cu_seqlens);
   s.prefix_lens = reinterpret_cast<const int32_t *>(base + L.prefix_lens);
   s.cu_items = reinterpret_cast<const int32_t *>(base + L.cu_items);

@@ -448,10 +448,11 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
   const __bf16 *kp = static_cast<const __bf16 *>(k);
   const __bf16 *vp = static_cast<const __bf16 *>(v);
   __bf16 *op = static_cast<__bf16 *>(o);
-  // Three kernels. Long runs of work (GQA groups of 4 or more and at least 8
-  // four-head workgroups per CU) take the pipelined loop with 64 query rows
-  // per wave: one wave per SIMD, so it cannot hide the fixed cost of starting
-  // a query tile behind another workgroup, but its loop is the fastest. Other
+  // Three kernels. Long runs of work (GQA groups of 4 or more, query tiles
+  // that visit 48 key tiles or more on average, and at least 8 four-head
+  // workgroups per CU) take the pipelined loop with 64 query rows per wave:
+  // one wave per SIMD, so it cannot hide the fixed cost of starting a query
+  // tile behind another workgroup, but its loop is the fastest. Other
   // even group sizes take the pipelined loop with 32 rows per wave, two waves
   // per SIMD (2 row blocks x 2 heads per workgroup); odd group sizes this
   // file's kernel (2 row blocks x 1 head, plain loop, two waves per SIMD).
@@ -462,7 +463,8 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
   const bool want_classic = force && std::strcmp(force, "classic") == 0;
   const bool want_pipe32 = force && std::strcmp(force, "pipe32") == 0;
   const bool pipe_fits = gsz % 2 == 0;
-  const bool pipe_pays = gsz % 4 == 0 && int64_t(seg.num_work) * (hq / 4) >= 8 * int64_t(device_cus());
+  const bool pipe_pays = gsz % 4 == 0 && int64_t(seg.num_visits) >= 48 * int64_t(seg.num_work) &&
+                         int64_t(seg.num_work) * (hq / 4) >= 8 * int64_t(device_cus());
   if (pipe_fits && (want_pipe || (pipe_pays && !want_classic && !want_pipe32)))
     return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, st);
   if (pipe_fits && !want_classic)

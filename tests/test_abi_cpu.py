@@ -34,8 +34,9 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # 8 int32 fields then 10 pointers
-    assert ctypes.sizeof(mis.MisSegments) == 8 * 4 + 10 * 8
+    # 9 int32 fields (padded to 8-byte alignment) then 10 pointers
+    assert mis.MisSegments.cu_seqlens.offset == 40
+    assert ctypes.sizeof(mis.MisSegments) == 40 + 10 * 8
 
 
 def _i32(a):

@@ -47,6 +47,8 @@ def _check_work_list(wl, seg, cls):
             seen[cu_tiles[r] + qt * nkt + kt] += 1
     assert (seen <= 1).all()
     assert ((seen == 1) == (cls != 0)).all()
+    # the visit count the attention dispatcher reads: every tile with a visible cell
+    assert seg.struct.num_visits == int((cls != 0).sum()) == sum(costs)
     assert all(costs[i] >= costs[i + 1] for i in range(len(costs) - 1))
     assert sorted(map(tuple, work[:, :2].tolist())) == sorted(
         (r, qt) for r in range(wl.num_requests)
