@@ -5,8 +5,8 @@ Run ``python gen_attn_loop.py`` in this directory after editing; the output
 is committed and the build does not run this script (a CPU test checks that
 the committed file matches what this script writes).
 
-What the block computes (one wave = 64 query rows of one head; the caller
-has set up everything the loop needs):
+What the block computes (one wave = 64 query rows of one head, or 32 in the
+QB1 variant; the caller has set up everything the loop needs):
 
   for each 64-key tile of the visit list (two 32-key sub-tiles each):
     S^T = K Q^T on v_mfma_f32_32x32x16_bf16, Eq. 4 mask on the tiles that
@@ -15,14 +15,16 @@ has set up everything the loop needs):
 The sub-tiles are software-pipelined: the step of sub-tile j issues the QK
 MFMAs of sub-tile j+1 and the PV MFMAs of sub-tile j-1 while the VALU turns
 S(j) into P(j), so the matrix cores and the vector ALU work side by side
-inside one wave (one wave per SIMD). The running maximum m of a row is only
-raised when a sub-tile's partial row sum exceeds 2^24 (the first visited
-sub-tile always does, because m starts at -1e30): then the exact maximum of
-the sub-tile is taken, O and the row sum are rescaled and P is recomputed.
+inside one wave. The running maximum m of a row is only raised when a
+sub-tile's largest P exceeds 2^24 (the first visited sub-tile always does,
+because m starts at -1e30): then the exact maximum of the sub-tile is taken,
+O and the row sum are rescaled (not on the query tile's first sub-tile,
+where both are still zero) and P is recomputed.
 Any m that was ever a real maximum keeps the result exact, because O and the
 row sum are scaled by the same exp2(-m).
 
-Register map (physical, clobbered by the block; see the constants below):
+Register map of the 64-row variant (physical, clobbered by the block;
+set_layout gives both variants' maps):
   v[0:31]    S_A   (S^T of a sub-tile, 2 query blocks x 16 fp32)
   v[32:63]   S_B
   v[64:79]   P_A   (P^T bf16, [qb][ks] 4 dwords each)
