@@ -156,7 +156,7 @@ def sweep(args) -> int:
     its own copy of the prefix, in one batched call (SIS). Both run the full
     step (segments, attention, label scores) on the same model shape as the
     single-request workload; the prefix is 744 tokens (the mean prompt length
-    the paper reports for its profile set) and each item 24 tokens plus its
+    From Generation to Scoring reports for its profile set) and each item 24 tokens plus its
     delimiter (the compact prompt).
     """
     import torch

@@ -110,7 +110,7 @@ int mis_segments_bytes(int32_t num_requests, const int32_t *cu_seqlens_h, int32_
                        int32_t block_m, int32_t block_n, size_t *bytes);
 
 /*
- * Build the segment descriptors of a packed MIS batch (paper §4.1: Eq. 3
+ * Build the segment descriptors of a packed MIS batch (From Generation to Scoring, §4.1: Eq. 3
  * packing, the reused position-id rule and the Eq. 4 mask; SGLang blog's
  * delimiter-closed items). Per-token ids, readout positions and tile classes
  * are computed by GPU kernels; the host validates the metadata, orders the
@@ -146,7 +146,7 @@ int mis_attention_tile_shape(mis_dtype dt, int32_t hq, int32_t hkv, int32_t head
 
 /*
  * MIS prefill attention: O = softmax(scale * Q K^T + M) V per query head,
- * M the Eq. 4 mask of paper §4.1 inside each request, no attention across
+ * M the Eq. 4 mask of From Generation to Scoring, §4.1 inside each request, no attention across
  * requests. Query head h reads KV head floor(h * hkv / hq) (contiguous GQA
  * groups). Key tiles with no visible cell are never loaded; per-cell masking
  * runs only in partly visible tiles.
@@ -179,7 +179,7 @@ int mis_attention_append(const mis_segments *seg, const void *q, const void *k, 
 
 /*
  * Rotary position embedding of Q and K in place, at the segment's position
- * ids (paper §4.1's position-id rule: prefix token u at u, the token at
+ * ids (From Generation to Scoring, §4.1's position-id rule: prefix token u at u, the token at
  * offset d inside any item at Lq + d), so each item is rotated as if it
  * followed the prefix alone and MIS equals single-item scoring with the
  * rotation applied. Dims i and i + D/2 (i < D/2) of every head row are turned
@@ -203,7 +203,7 @@ int mis_score_workspace_bytes(int32_t num_items, int32_t vocab, int32_t num_labe
                               int32_t hidden, mis_dtype dt, size_t *bytes);
 
 /*
- * Label scores of every item (paper §3.3, Eq. 2; JEV post, Score API with
+ * Label scores of every item (From Generation to Scoring, §3.3, Eq. 2; JEV post, Score API with
  * label_token_ids and apply_softmax; full-vocabulary normalisation is kept).
  * For item n, h_n = hidden[seg->readout_pos[n]] and z_n = lm_head h_n over
  * the whole vocabulary. Without apply_softmax, scores[n,k] = z_n[label_k] -
@@ -228,7 +228,7 @@ int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden
  * each entry of positions_h, from hidden[positions_h[r]], computed exactly as
  * in mis_score_labels. This serves several readout markers per item (setwise
  * scoring, JEV post's score extraction positions) and graded multi-class
- * labels (paper §9: several single-token class labels normalised together,
+ * labels (From Generation to Scoring, §9: several single-token class labels normalised together,
  * with apply_softmax).
  *
  * positions_h: host [num_rows], each in [0, num_tokens), read before return.

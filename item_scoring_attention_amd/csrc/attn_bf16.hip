@@ -4,8 +4,8 @@
 // From Generation to Scoring, §4.1, Eq. 4: a prefix row sees the prefix up to
 // itself; an item row sees the whole prefix and its own item up to itself.
 // Flash-style online softmax: key tiles are streamed through LDS and key
-// tiles that hold only other items' tokens are never visited (the paper's
-// §4.3 remark that the MIS kernels skip fully masked tiles; the SGLang blog's
+// tiles that hold only other items' tokens are never visited (From Generation to Scoring,
+// §4.3: the remark that the MIS kernels skip fully masked tiles; the SGLang blog's
 // list of FlashInfer changes).
 //
 // Work decomposition

@@ -25,10 +25,10 @@ What it computes, from the pages' own statement of the method:
   selection does not remove the full projection or normalisation). The
   label columns of the log-softmax come back in the requested label order.
   With ``apply_softmax`` the K label logits are renormalised among
-  themselves (Eq. 2 of the paper for the YES/NO pair; the Score API's
+  themselves (Eq. 2 of From Generation to Scoring for the YES/NO pair; the Score API's
   apply_softmax flag in the JEV post).
 * SIS. Single-item scoring runs every [q; c_i] alone under an ordinary
-  causal mask; MIS must give the same item rows and scores (paper §4.1: the
+  causal mask; MIS must give the same item rows and scores (From Generation to Scoring, §4.1: the
   mask and reused positions give the item's last token the context it has
   in [q; c_i]; Table 1's release check).
 * Rotary embedding (the step before attention). The pages fix the positions
@@ -65,7 +65,7 @@ def as_f64(x: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# segments (paper §4.1, Eq. 3 and the position-id rule; blog's delimiter format)
+# segments (From Generation to Scoring, §4.1, Eq. 3 and the position-id rule; blog's delimiter format)
 # --------------------------------------------------------------------------
 
 
@@ -110,7 +110,7 @@ def request_item_ids(seg: Dict[str, np.ndarray], cu_seqlens, r: int) -> np.ndarr
 
 
 # --------------------------------------------------------------------------
-# mask (paper §4.1, Eq. 4)
+# mask (From Generation to Scoring, §4.1, Eq. 4)
 # --------------------------------------------------------------------------
 
 
@@ -320,7 +320,7 @@ def sis_rope_attention(q, k, v, cu_seqlens, prefix_lens, cu_items, item_starts, 
 
 
 # --------------------------------------------------------------------------
-# label scores (paper §3.3 Eq. 2; JEV post's Score API and full-vocab normalisation)
+# label scores (From Generation to Scoring, §3.3 Eq. 2; JEV post's Score API and full-vocab normalisation)
 # --------------------------------------------------------------------------
 
 
