@@ -11,6 +11,9 @@ The computation lives in ``libmis.so`` (HIP kernels behind the C ABI of
 * ``mis_score_labels``: readout gather, LM-head contraction and full-vocab
   logsumexp, writing one label-score row per item (``mis_score_labels_at``:
   at any token rows, e.g. several readout markers per item).
+
+``pack_requests`` (host only) turns queries, candidate items and a delimiter
+token into the packed token ids and the offsets ``mis_build_segments`` takes.
 """
 from ._lib import (  # noqa: F401
     LIB_PATH,
@@ -42,3 +45,4 @@ from ._lib import (  # noqa: F401
     mis_segments_bytes,
     version,
 )
+from .pack import Packed, build_packed_segments, pack_requests  # noqa: F401,E402

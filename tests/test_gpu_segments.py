@@ -109,3 +109,19 @@ def test_many_builds_in_flight_keep_their_own_metadata():
         assert np.array_equal(host(seg.array("readout_pos")), so["readout_pos"])
         cls, _ = oracle.tile_classes(wl.cu_seqlens, so["item_id"], seg.block_m, seg.block_n)
         assert np.array_equal(host(seg.array("tile_class")), cls)
+
+
+def test_packed_batch_builds_the_packers_readout_positions():
+    # the token-level packer's offsets through the GPU builder
+    from item_scoring_attention_amd import build_packed_segments, pack_requests
+    rng = np.random.default_rng(11)
+    reqs = [(rng.integers(0, 50000, size=int(rng.integers(1, 300))),
+             [rng.integers(0, 50000, size=int(rng.integers(0, 40))) for _ in range(int(rng.integers(0, 30)))])
+            for _ in range(6)]
+    p = pack_requests(reqs, delimiter_id=50001)
+    seg = build_packed_segments(p, 64, 64)
+    assert np.array_equal(host(seg.array("readout_pos")), p.readout_pos)
+    so = oracle.build_segments(p.cu_seqlens, p.prefix_lens, p.cu_items, p.item_starts)
+    assert np.array_equal(host(seg.array("item_id")), so["item_id"])
+    assert np.array_equal(host(seg.array("pos_id")), so["pos_id"])
+
