@@ -323,10 +323,34 @@ int mis_build_segments(int32_t B, const int32_t *cu_seqlens_h, const int32_t *pr
   s.work = reinterpret_cast<const int32_t *>(base + L.work);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = stage_ring().upload(dev_buf, img.data(), L.stage_end, st);
-  if (e != hipSuccess) return hip_fail(e, "staging segment metadata");
-  e = mis::launch_segments(s, reinterpret_cast<const int32_t *>(base + L.item_starts), st);
-  if (e != hipSuccess) return hip_fail(e, "segment builder launch");
+  // Small batches: the staged arrays travel in the builder's kernel
+  // arguments, which saves a separate copy and its launch; larger ones go
+  // through pinned memory and one copy.
+  const size_t counts[mis::kInlineArrays] = {size_t(B) + 1, size_t(B), size_t(B) + 1, size_t(B) + 1, size_t(N),
+                                             4 * size_t(work)};
+  const size_t offs[mis::kInlineArrays] = {L.cu_seqlens, L.prefix_lens, L.cu_items, L.cu_tiles, L.item_starts, L.work};
+  size_t inline_words = 0;
+  for (size_t c : counts) inline_words += c;
+  hipError_t e;
+  if (inline_words <= size_t(mis::kInlineWords)) {
+    mis::InlineMeta meta{};
+    mis::InlineLayout lay{};
+    int32_t at = 0;
+    for (int a = 0; a < mis::kInlineArrays; ++a) {
+      lay.src[a] = at;
+      lay.dst[a] = int32_t(offs[a] / sizeof(int32_t));
+      lay.len[a] = int32_t(counts[a]);
+      if (counts[a]) std::memcpy(meta.w + at, img.data() + offs[a], counts[a] * sizeof(int32_t));
+      at += int32_t(counts[a]);
+    }
+    e = mis::launch_segments_inline(s, lay, meta, static_cast<int32_t *>(dev_buf), st);
+    if (e != hipSuccess) return hip_fail(e, "segment builder launch");
+  } else {
+    e = stage_ring().upload(dev_buf, img.data(), L.stage_end, st);
+    if (e != hipSuccess) return hip_fail(e, "staging segment metadata");
+    e = mis::launch_segments(s, reinterpret_cast<const int32_t *>(base + L.item_starts), st);
+    if (e != hipSuccess) return hip_fail(e, "segment builder launch");
+  }
   *out = s;
   return ok();
 }

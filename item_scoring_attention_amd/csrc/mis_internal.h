@@ -29,6 +29,22 @@ struct LabelArgs {
 hipError_t launch_segments(const mis_segments &seg, const int32_t *item_starts_dev,
                            hipStream_t stream);
 
+// Metadata small enough to travel in the builder's kernel arguments: the
+// staged arrays packed back to back (kInlineWords int32 at most) and, per
+// array, its word offset there, its word offset in the segment buffer and
+// its length. Array order: cu_seqlens, prefix_lens, cu_items, cu_tiles,
+// item_starts, work.
+constexpr int kInlineWords = 768;
+constexpr int kInlineArrays = 6;
+struct InlineMeta {
+  int32_t w[kInlineWords];
+};
+struct InlineLayout {
+  int32_t src[kInlineArrays], dst[kInlineArrays], len[kInlineArrays];
+};
+hipError_t launch_segments_inline(const mis_segments &seg, const InlineLayout &lay, const InlineMeta &meta,
+                                  int32_t *stage, hipStream_t stream);
+
 // items_only != 0: rows of query tiles that hold prefix rows only are not
 // computed (appending items to a cached prefix).
 hipError_t launch_attention_f32(const mis_segments &seg, const float *q, const float *k,

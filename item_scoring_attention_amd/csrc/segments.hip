@@ -47,9 +47,9 @@ __device__ __forceinline__ int64_t sum_clip(int64_t lo, int64_t hi, int64_t m0, 
   return total;
 }
 
-// One launch, three roles by block range: tokens, items, tiles. No role reads
+// The three roles by block range: tokens, items, tiles. No role reads
 // another role's output, so they need no ordering.
-__global__ __launch_bounds__(256) void builder_kernel(
+__device__ __forceinline__ void build_roles(
     int B, int T, int N, int num_tiles, int bm, int bn, int tok_blocks, int item_blocks,
     const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ prefix_lens,
     const int32_t *__restrict__ cu_items, const int32_t *__restrict__ item_starts,
@@ -113,7 +113,50 @@ __global__ __launch_bounds__(256) void builder_kernel(
   tile_class[g] = visible == 0 ? int8_t(0) : (visible == cells ? int8_t(2) : int8_t(1));
 }
 
+// Metadata already staged in device memory by a copy.
+__global__ __launch_bounds__(256) void builder_kernel(
+    int B, int T, int N, int num_tiles, int bm, int bn, int tok_blocks, int item_blocks,
+    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ prefix_lens,
+    const int32_t *__restrict__ cu_items, const int32_t *__restrict__ item_starts,
+    const int32_t *__restrict__ cu_tiles, int32_t *__restrict__ item_id, int32_t *__restrict__ pos_id,
+    int32_t *__restrict__ item_begin, int32_t *__restrict__ readout_pos, int8_t *__restrict__ tile_class) {
+  build_roles(B, T, N, num_tiles, bm, bn, tok_blocks, item_blocks, cu_seqlens, prefix_lens, cu_items,
+              item_starts, cu_tiles, item_id, pos_id, item_begin, readout_pos, tile_class);
+}
+
+// Small batches: the metadata travels in the kernel arguments (no separate
+// host-to-device copy and launch). Every thread first copies its share of
+// the arrays to their places in the segment buffer (the later kernels read
+// them there), then runs its role on the argument copy.
+__global__ __launch_bounds__(256) void builder_inline_kernel(
+    int B, int T, int N, int num_tiles, int bm, int bn, int tok_blocks, int item_blocks, InlineLayout lay,
+    InlineMeta meta, int32_t *__restrict__ stage, int32_t *__restrict__ item_id, int32_t *__restrict__ pos_id,
+    int32_t *__restrict__ item_begin, int32_t *__restrict__ readout_pos, int8_t *__restrict__ tile_class) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nthreads = gridDim.x * blockDim.x;
+#pragma unroll
+  for (int a = 0; a < kInlineArrays; ++a)
+    for (int i = g; i < lay.len[a]; i += nthreads) stage[lay.dst[a] + i] = meta.w[lay.src[a] + i];
+  const int32_t *w = meta.w;
+  build_roles(B, T, N, num_tiles, bm, bn, tok_blocks, item_blocks, w + lay.src[0], w + lay.src[1], w + lay.src[2],
+              w + lay.src[4], w + lay.src[3], item_id, pos_id, item_begin, readout_pos, tile_class);
+}
+
 }  // namespace
+
+hipError_t launch_segments_inline(const mis_segments &seg, const InlineLayout &lay, const InlineMeta &meta,
+                                  int32_t *stage, hipStream_t st) {
+  constexpr int kThreads = 256;
+  const int tok_blocks = (seg.total_tokens + kThreads - 1) / kThreads;
+  const int item_blocks = (seg.total_items + kThreads - 1) / kThreads;
+  const int tile_blocks = (seg.num_tiles + kThreads - 1) / kThreads;
+  builder_inline_kernel<<<tok_blocks + item_blocks + tile_blocks, kThreads, 0, st>>>(
+      seg.num_requests, seg.total_tokens, seg.total_items, seg.num_tiles, seg.block_m, seg.block_n,
+      tok_blocks, item_blocks, lay, meta, stage, const_cast<int32_t *>(seg.item_id),
+      const_cast<int32_t *>(seg.pos_id), const_cast<int32_t *>(seg.item_begin),
+      const_cast<int32_t *>(seg.readout_pos), const_cast<int8_t *>(seg.tile_class));
+  return hipGetLastError();
+}
 
 hipError_t launch_segments(const mis_segments &seg, const int32_t *item_starts, hipStream_t st) {
   constexpr int kThreads = 256;
