@@ -100,6 +100,15 @@ struct LoopArgs {
     [rb4] "s"(x.rb4), [nrec] "s"(x.nrec), [wsoff] "s"(x.wsoff), [wlds] "s"(x.wlds), [c] "s"(x.c)                  \
   : MIS_ATTN_LOOP_CLOBBERS_QB1
 
+// The ring's first loads (a block of their own, issued with the kernel's own
+// loads); the loop block then finds them landed.
+#define MIS_ATTN_PROLOGUE_OPERANDS                                                                                  \
+  ::[ko0] "v"(x.ko[0]), [ko1] "v"(x.ko[1]), [ko2] "v"(x.ko[2]), [ko3] "v"(x.ko[3]), [vo] "v"(x.vo),               \
+    [nvis] "s"(x.nvis), [a_end] "s"(x.a_end), [b_start] "s"(x.b_start), [kb_lo] "s"(x.kb_lo), [kb_hi] "s"(x.kb_hi), \
+    [vb_lo] "s"(x.vb_lo), [vb_hi] "s"(x.vb_hi), [rb64] "s"(x.rb64), [rb4] "s"(x.rb4), [nrec] "s"(x.nrec),        \
+    [wsoff] "s"(x.wsoff), [wlds] "s"(x.wlds)                                                                      \
+  : MIS_ATTN_PROLOGUE_CLOBBERS
+
 // Runs the whole key-tile loop; O^T (unnormalised) and the row sums of the
 // lane's two query rows come back. DPW = LDS-direct loads per wave, tile and operand (16 / HP).
 template <int DPW>
@@ -185,67 +194,20 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
   const int row0 = qt * BM + 32 * tb;  // first query row of the wave
 
   const int64_t q_stride = int64_t(hq) * D;
-  // Q^T operands of the wave's query blocks; rows past the request end read as zeros.
-  f32x32 qv[QB];
-  {
-    const uint32_t q_bytes = uint32_t(Tr) * uint32_t(q_stride) * 2u - uint32_t(head) * D * 2u;
-    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16 *>(q + int64_t(base) * q_stride + int64_t(head) * D), 0, q_bytes, kRsrcWord3);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const uint32_t qo = uint32_t(row0 + 32 * qb + ql) * uint32_t(q_stride) * 2u + 16u * g;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const f32x4 f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qo + 32u * kk, 0, 0));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qv[qb][4 * kk + e] = f[e];
-      }
-    }
-  }
+  const int64_t kv_stride = int64_t(hkv) * D;
+  const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
+
+  // The V stages start as zeros: rows past the request end are not written
+  // by the loads, and the first PV step multiplies a zero P with the last
+  // stage. Done first, so the ring's first loads can go out with the kernel's
+  // own (below) once every wave's stores are in LDS.
+  for (int i = tid; i < STAGES * TILE / 8; i += 64 * NW)
+    *reinterpret_cast<uint4 *>(&smem[STAGES * TILE + i * 8]) = make_uint4(0, 0, 0, 0);
 
   LoopArgs x;
   x.nvis = n_visit;
   x.a_end = a_end;
   x.b_start = b_start;
-  // Visits before a_full are fully visible tiles (class 2) that end inside
-  // the request; the mask runs on every visit from a_full on.
-  {
-    int first = n_visit;
-#pragma unroll 4
-    for (int i0 = 0; i0 < n_visit; i0 += 64) {
-      const int idx = i0 + lane;
-      if (idx < n_visit) {
-        const int kt = idx < a_end ? idx : b_start + (idx - a_end);
-        if ((tile_class[cls_base + kt] != 2) | (kt * BN + BN > Tr)) first = min(first, idx);
-      }
-    }
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) first = min(first, __shfl_xor(first, s));
-    x.a_full = __builtin_amdgcn_readfirstlane(first);
-  }
-
-  // Mask bounds of the lane's query rows (j = row0 + query block * 32 + lane % 32);
-  // the lane's keys in a sub-tile are key0 + 8 (a / 4) + a % 4 + 4 g.
-  x.rjt[1] = x.rjb[1] = 0;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int j = row0 + 32 * qb + ql;
-    // an item row at offset d of its item has position id lq + d (the
-    // reused positions), so its item starts at row j - d
-    const int jb = (j < Tr && j >= lq) ? j - (pos_id[base + j] - lq) : 0;
-    x.rjt[qb] = min(j, Tr - 1) - 4 * g;
-    x.rjb[qb] = jb - 4 * g;
-  }
-  x.rlq = lq - 4 * g;
-
-  const int64_t kv_stride = int64_t(hkv) * D;
-  const uint32_t kv_row_bytes = uint32_t(kv_stride) * 2u;
-
-  // The V stages start as zeros: rows past the request end are not written
-  // by the loads, and the first PV step multiplies a zero P with the last stage.
-  for (int i = tid; i < STAGES * TILE / 8; i += 64 * NW)
-    *reinterpret_cast<uint4 *>(&smem[STAGES * TILE + i * 8]) = make_uint4(0, 0, 0, 0);
-
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t vlds0 = lds0 + uint32_t(STAGES * TILE * 2);  // start of the V stages
   // K fragment of 16-dim step kk: key ql (+32 for the second key block), chunk 2 kk + g.
@@ -288,8 +250,80 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
   x.wsoff = wrow * kv_row_bytes;
   x.wlds = lds0 + wrow * 256u;
   x.c = c;
+  x.rlq = lq - 4 * g;
 
-  __syncthreads();  // V zero fill done before any load lands in LDS
+  // Every wave's zero stores are in LDS before any load lands there (an LDS
+  // wait and a barrier; no fence, which would wait for vector memory too).
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The kernel's own loads, issued together, their results used only after
+  // the ring's first loads are out too (one round trip for all of them).
+  // Q^T operands of the wave's query blocks; rows past the request end read as zeros.
+  f32x32 qv[QB];
+  {
+    const uint32_t q_bytes = uint32_t(Tr) * uint32_t(q_stride) * 2u - uint32_t(head) * D * 2u;
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16 *>(q + int64_t(base) * q_stride + int64_t(head) * D), 0, q_bytes, kRsrcWord3);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const uint32_t qo = uint32_t(row0 + 32 * qb + ql) * uint32_t(q_stride) * 2u + 16u * g;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const f32x4 f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qo + 32u * kk, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[qb][4 * kk + e] = f[e];
+      }
+    }
+  }
+  // class of visit `lane` (lanes past the last visit read visit 0's tile)
+  const int kt0 = lane < n_visit ? (lane < a_end ? lane : b_start + (lane - a_end)) : (a_end > 0 ? 0 : b_start);
+  const int tc0 = tile_class[cls_base + kt0];
+  // position ids of the lane's query rows (rows past the request end read the last row)
+  int pos[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) pos[qb] = pos_id[base + min(row0 + 32 * qb + ql, Tr - 1)];
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  if constexpr (QB == 1)
+    asm volatile(MIS_ATTN_PROLOGUE_TEXT_QB1 MIS_ATTN_PROLOGUE_OPERANDS);
+  else if constexpr (BN / HP / 4 == 4)
+    asm volatile(MIS_ATTN_PROLOGUE_TEXT_DPW4 MIS_ATTN_PROLOGUE_OPERANDS);
+  else
+    asm volatile(MIS_ATTN_PROLOGUE_TEXT_DPW8 MIS_ATTN_PROLOGUE_OPERANDS);
+#pragma clang diagnostic pop
+
+  // Visits before a_full are fully visible tiles (class 2) that end inside
+  // the request; the mask runs on every visit from a_full on.
+  {
+    int first = n_visit;
+    if (lane < n_visit && ((tc0 != 2) | (kt0 * BN + BN > Tr))) first = lane;
+    for (int i0 = 64; i0 < n_visit; i0 += 64) {
+      const int idx = i0 + lane;
+      if (idx < n_visit) {
+        const int kt = idx < a_end ? idx : b_start + (idx - a_end);
+        if ((tile_class[cls_base + kt] != 2) | (kt * BN + BN > Tr)) first = min(first, idx);
+      }
+    }
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) first = min(first, __shfl_xor(first, s));
+    x.a_full = __builtin_amdgcn_readfirstlane(first);
+  }
+
+  // Mask bounds of the lane's query rows (j = row0 + query block * 32 + lane % 32);
+  // the lane's keys in a sub-tile are key0 + 8 (a / 4) + a % 4 + 4 g.
+  x.rjt[1] = x.rjb[1] = 0;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int j = row0 + 32 * qb + ql;
+    // an item row at offset d of its item has position id lq + d (the
+    // reused positions), so its item starts at row j - d
+    const int jb = (j < Tr && j >= lq) ? j - (pos[qb] - lq) : 0;
+    x.rjt[qb] = min(j, Tr - 1) - 4 * g;
+    x.rjb[qb] = jb - 4 * g;
+  }
 
   f32x32 o0, o1, o2, o3;
   float l0, l1 = 1.f;

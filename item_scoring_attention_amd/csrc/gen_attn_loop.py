@@ -459,19 +459,8 @@ def loop_block(dpw: int, stages: int) -> list[str]:
     b.emit(f"v_mov_b32 {vr(VNINF)}, 0xff800000")
     b.emit(f"s_mov_b32 {sr(S_LIM)}, 0x4b800000")  # 2^24
     b.emit(f"s_mov_b32 {sr(S_T)}, 0")
-    # ---- prologue: the loads the barriers of visits -STAGES+1 .. -1 would
-    # have issued, K(0) first: K(0), K(1), V(0), then (three stages) K(2),
-    # V(1). Only K(0) is waited for here (QK(0) -> S_A); the barrier of visit
-    # 0 waits for K(1) and V(0) like any other.
-    order = [(0, True), (1, True), (0, False)] + ([(2, True), (1, False)] if stages == 3 else [])
-    for v, is_k in order:
-        rsrc, so = (S_RSRC, S_SO) if is_k else (S_VRSRC, S_VSO)
-        dma_setup(b, v, is_k, rsrc)
-        lds = k_off(v) if is_k else v_lds(v, stages)
-        for g in dma_groups(is_k, rsrc, so, lds, dpw):
-            for ln in g:
-                b.emit(ln)
-    b.emit(f"s_waitcnt vmcnt({dpw * (len(order) - 1)})")
+    # ---- the prologue loads (prologue_block) have landed: the block's first
+    # wait covers them. Every wave's share of K(0) is in LDS after the barrier.
     b.emit("s_barrier")
     b.reset_ds()
     for ds in range(8):
@@ -556,6 +545,30 @@ def loop_block(dpw: int, stages: int) -> list[str]:
     return [ln for ln in b.lines if ln]
 
 
+def prologue_order(stages: int) -> list[tuple[int, bool]]:
+    """The loads the barriers of visits -STAGES+1 .. -1 would have issued, K(0)
+    first: K(0), K(1), V(0), then (three stages) K(2), V(1)."""
+    return [(0, True), (1, True), (0, False)] + ([(2, True), (1, False)] if stages == 3 else [])
+
+
+def prologue_block(dpw: int, stages: int) -> list[str]:
+    """The ring's first loads as a block of their own. The kernel issues it
+    right after its own loads (Q, tile classes, position ids) and before it
+    uses any of their results, so all of them travel in one round trip; the
+    kernel's wait for its own loads then also covers these (loads complete in
+    order), and the loop block starts with every prologue load landed."""
+    b = Block()
+    b.emit(f"s_mov_b32 {sr(S_T)}, 0")
+    for v, is_k in prologue_order(stages):
+        rsrc, so = (S_RSRC, S_SO) if is_k else (S_VRSRC, S_VSO)
+        dma_setup(b, v, is_k, rsrc)
+        lds = k_off(v) if is_k else v_lds(v, stages)
+        for g in dma_groups(is_k, rsrc, so, lds, dpw):
+            for ln in g:
+                b.emit(ln)
+    return [ln for ln in b.lines if ln]
+
+
 def clobbers() -> list[str]:
     regs = [f'"v{i}"' for i in range(NUM_V)]
     regs += [f'"s{i}"' for i in SGPRS]
@@ -587,10 +600,16 @@ def render() -> str:
         out.append(f"#define MIS_ATTN_LOOP_TEXT_{name} \\")
         out.append(" \\\n".join(text))
         out.append("")
+        text = [f'  "{ln}\\n"' for ln in prologue_block(dpw, stages)]
+        out.append(f"#define MIS_ATTN_PROLOGUE_TEXT_{name} \\")
+        out.append(" \\\n".join(text))
+        out.append("")
     set_layout(2)
     out.append("#define MIS_ATTN_LOOP_CLOBBERS " + ", ".join(clobbers()))
     set_layout(1)
     out.append("#define MIS_ATTN_LOOP_CLOBBERS_QB1 " + ", ".join(clobbers()))
+    out.append("#define MIS_ATTN_PROLOGUE_CLOBBERS " + ", ".join(
+        [f'"s{i}"' for i in SGPRS] + ['"scc"', '"m0"', '"memory"']))
     set_layout(2)
     out.append("")
     return "\n".join(out)
