@@ -23,6 +23,11 @@ where both are still zero) and P is recomputed.
 Any m that was ever a real maximum keeps the result exact, because O and the
 row sum are scaled by the same exp2(-m).
 
+The ring's first loads (K(0), K(1), V(0), and with three stages K(2), V(1))
+are a second, small block (MIS_ATTN_PROLOGUE_TEXT_*): the kernel issues it
+right after its own loads of Q, tile classes and position ids, so all of them
+take one round trip, and the loop block starts with them landed.
+
 Register map of the 64-row variant (physical, clobbered by the block;
 set_layout gives both variants' maps):
   v[0:31]    S_A   (S^T of a sub-tile, 2 query blocks x 16 fp32)
