@@ -69,6 +69,9 @@ def test_f32_d128_and_gqa():
     ([129, 1], [[1, 1, 1], []], 16, 8),
     ([300], [[17] * 12], 4, 4),  # G = 1 (MHA) uses the one-head workgroup
     ([64, 63], [[64], [1, 1]], 6, 2),  # odd group size (3)
+    # 67 visits per item tile: the first partly visible tile (the prefix's
+    # last) is visit 65, past the 64 a wave's lanes cover in one pass
+    ([4200], [[5, 9, 40]], 8, 2),
 ])
 def test_bf16_small_shapes_all_elements(shape):
     p, it, hq, hkv = shape
