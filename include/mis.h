@@ -114,7 +114,9 @@ int mis_segments_bytes(int32_t num_requests, const int32_t *cu_seqlens_h, int32_
  * packing, the reused position-id rule and the Eq. 4 mask; SGLang blog's
  * delimiter-closed items). Per-token ids, readout positions and tile classes
  * are computed by GPU kernels; the host validates the metadata, orders the
- * query tiles longest first and stages everything with one copy.
+ * query tiles longest first and stages everything in the builder kernel's
+ * arguments (batches whose staged arrays fit 768 words) or with one copy
+ * through pinned host memory.
  *
  * In (host, read before return; the caller may free them afterwards):
  *   cu_seqlens_h[B+1]  non-decreasing, cu_seqlens_h[0] = 0, every T_r >= 1
