@@ -71,3 +71,15 @@ def test_append_equals_prefill_item_rows_bit_for_bit_single_request_workload():
     full = host(mis.mis_attention_prefill(seg, qd, kd, vd))
     items, _ = _item_mask(wl)
     assert np.array_equal(host(o)[items], full[items])
+
+
+def test_append_equals_prefill_item_rows_bit_for_bit_long_visit_lists():
+    # a 4200-token prefix: item tiles visit 67 key tiles, the first partly
+    # visible one (the prefix's last) past the first 64
+    wl = workloads.from_lengths("append-long", [4200, 130], [[5, 9, 40], [7, 7]], hq=8, hkv=2, d=128, seed=23)
+    say(f"[append] {wl.name} T={wl.total_tokens}")
+    q, k, v = workloads.qkv(wl)
+    seg, qd, kd, vd, o = _append(wl, q, k, v)
+    full = host(mis.mis_attention_prefill(seg, qd, kd, vd))
+    items, _ = _item_mask(wl)
+    assert np.array_equal(host(o)[items], full[items])
