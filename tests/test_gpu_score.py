@@ -81,9 +81,11 @@ def test_long_prefix_config_sampled_items():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("n_items,vocab", [(1, 1000), (37, 129), (65, 1000), (200, 300), (300, 1)])
+@pytest.mark.parametrize("n_items,vocab", [(1, 1000), (32, 1000), (37, 129), (64, 2000), (65, 1000),
+                                            (160, 700), (200, 300), (257, 300), (300, 1)])
 def test_item_and_vocab_edges(dtype, n_items, vocab):
-    # ragged vocabulary tiles, item tiles with a tail, labels at both vocabulary ends
+    # ragged vocabulary tiles, item tiles with a tail or exactly full (32, 64,
+    # 160 = 5 x 32 items; 257 one past 8 x 32), labels at both vocabulary ends
     lens = [3] * n_items
     wl = workloads.from_lengths("edge", [10], [lens], dtype=dtype, hq=4, hkv=2, d=128, hidden=64,
                                 vocab=vocab, num_labels=1)
