@@ -156,8 +156,11 @@ int mis_attention_tile_shape(mis_dtype dt, int32_t hq, int32_t hkv, int32_t head
  * q [T, hq, D], k and v [T, hkv, D], o [T, hq, D]: device, token-major,
  * contiguous, element type dt (bf16 uses fp32 accumulation and fp32 softmax;
  * P and O are rounded to bf16 to nearest even). softmax_scale <= 0 selects
- * 1/sqrt(D). D must be 64 or 128; hq % hkv == 0.
- * Errors: ARG, UNSUPPORTED (D, dt, or seg tile shape), HIP.
+ * 1/sqrt(D). D must be 64 or 128; hq % hkv == 0. With bf16 every request
+ * must satisfy (T_r + 64) * hq * D * 2 < 2^32 bytes (the kernels address a
+ * request's rows with 32-bit offsets).
+ * Errors: ARG, UNSUPPORTED (D, dt, seg tile shape, or a request beyond that
+ * range), HIP.
  */
 int mis_attention_prefill(const mis_segments *seg, const void *q, const void *k, const void *v,
                           void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
@@ -218,7 +221,8 @@ int mis_score_workspace_bytes(int32_t num_items, int32_t vocab, int32_t num_labe
  * input order), column k = label_ids_h[k]; may be NULL when N = 0 (the call
  * then only validates its arguments). ws/ws_bytes: device workspace of
  * at least mis_score_workspace_bytes.
- * Errors: ARG, LABEL, WORKSPACE, UNSUPPORTED, HIP.
+ * Errors: ARG, LABEL, WORKSPACE, UNSUPPORTED (bf16 with H % 32 != 0, or H
+ * above 4194304), HIP.
  */
 int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden_size,
                      const void *lm_head, int32_t vocab, mis_dtype dt, const int32_t *label_ids_h,

@@ -386,6 +386,14 @@ int attention_call(const mis_segments *seg, const void *q, const void *k, const 
   if (seg->total_tokens < 1 || !seg->work || !seg->tile_class || !seg->item_id)
     return fail(MIS_ERR_ARG, "seg is not a built segment descriptor");
   if (!std::isfinite(softmax_scale)) return fail(MIS_ERR_ARG, "softmax_scale is not finite");
+  // The bf16 kernels address a request's Q, K and V rows with 32-bit byte
+  // offsets from the request start (up to the end of its last 64-row tile).
+  if (dt == MIS_BF16 &&
+      (uint64_t(seg->max_seqlen) + 64) * uint64_t(hq) * uint64_t(head_dim) * 2u >= (uint64_t(1) << 32))
+    return fail(MIS_ERR_UNSUPPORTED,
+                "a request of %d tokens with %d query heads of %d dims exceeds the 4 GiB per-request range of the "
+                "bf16 kernels",
+                seg->max_seqlen, hq, head_dim);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = dt == MIS_BF16
@@ -461,6 +469,9 @@ int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden
   if (ws_bytes < need) return fail(MIS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, need);
   if (dt == MIS_BF16 && hidden_size % 32)
     return fail(MIS_ERR_UNSUPPORTED, "bf16 scoring needs hidden_size %% 32 == 0 (got %d)", hidden_size);
+  // a vocabulary tile's LM-head rows are addressed with 32-bit byte offsets
+  if (hidden_size > (1 << 22))
+    return fail(MIS_ERR_UNSUPPORTED, "hidden_size %d is above the 4194304 the scoring kernels address", hidden_size);
   if (seg->total_items == 0) return ok();
   if (!seg->readout_pos) return fail(MIS_ERR_ARG, "seg is not a built segment descriptor");
   mis::LabelArgs la{};
@@ -493,6 +504,9 @@ int mis_score_labels_at(const int32_t *positions_h, int32_t num_rows, int32_t nu
   if (ws_bytes < need) return fail(MIS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, need);
   if (dt == MIS_BF16 && hidden_size % 32)
     return fail(MIS_ERR_UNSUPPORTED, "bf16 scoring needs hidden_size %% 32 == 0 (got %d)", hidden_size);
+  // a vocabulary tile's LM-head rows are addressed with 32-bit byte offsets
+  if (hidden_size > (1 << 22))
+    return fail(MIS_ERR_UNSUPPORTED, "hidden_size %d is above the 4194304 the scoring kernels address", hidden_size);
   if (num_rows == 0) return ok();
   const size_t off = score_ws_positions_offset(size_t(num_rows), size_t(mis::score_vocab_tiles(vocab)), num_labels);
   int32_t *pos_dev = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(ws) + off);

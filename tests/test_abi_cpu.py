@@ -139,11 +139,17 @@ def test_attention_argument_errors():
     assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 4, 128, float("nan")) == mis.MIS_ERR_ARG
     s2 = _fake_seg(bm=32)
     assert call(ctypes.byref(s2), p, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_UNSUPPORTED
+    # bf16 kernels address a request with 32-bit byte offsets: (T_r + 64) x hq x D x 2 < 4 GiB
+    s3 = _fake_seg()
+    s3.max_seqlen = 262080  # + 64 = 2^18 rows of 64 heads x 128 dims x 2 bytes = 4 GiB
+    assert call(ctypes.byref(s3), p, mis.MIS_BF16, 64, 8, 128) == mis.MIS_ERR_UNSUPPORTED
+    assert "4 GiB" in mis.last_error()
     # the item-rows-only entry point runs the same host checks
     call = lambda seg, q, dt, hq, hkv, d, sc=0.0: lib.mis_attention_append(seg, q, p, p, p, dt, hq, hkv, d, sc, None)
     assert call(None, p, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_ARG
     assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 3, 128) == mis.MIS_ERR_ARG
     assert call(ctypes.byref(s2), p, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_UNSUPPORTED
+    assert call(ctypes.byref(s3), p, mis.MIS_BF16, 64, 8, 128) == mis.MIS_ERR_UNSUPPORTED
 
 
 def test_score_argument_errors():
@@ -164,6 +170,7 @@ def test_score_argument_errors():
     assert call([-1, 5], 2) == mis.MIS_ERR_LABEL
     assert call([3, 7], 2, ws_bytes=need - 1) == mis.MIS_ERR_WORKSPACE
     assert call([3, 7], 2, H=100) == mis.MIS_ERR_UNSUPPORTED
+    assert call([3, 7], 2, H=(1 << 22) + 32) == mis.MIS_ERR_UNSUPPORTED  # beyond 32-bit row offsets
     assert call([], 2) == mis.MIS_ERR_ARG
     assert lib.mis_score_labels(None, p, 256, p, 1000, mis.MIS_BF16, None, 2, 0, p, p, need,
                                 None) == mis.MIS_ERR_ARG
