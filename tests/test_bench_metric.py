@@ -1,0 +1,47 @@
+"""The headline metric's work count: bench.py's unmasked (query, key) pairs,
+which set the attention FLOPs of every bench line, against a count of the
+visible cells of the oracle's explicit Eq. 4 mask (From Generation to
+Scoring, §4.1), request by request. CPU only.
+"""
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import workloads
+
+
+def _mask_pairs(wl) -> int:
+    so = oracle.build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts)
+    ids = so["item_id"]
+    total = 0
+    for r in range(wl.num_requests):
+        a, b = int(wl.cu_seqlens[r]), int(wl.cu_seqlens[r + 1])
+        total += oracle.visible_pairs(ids[a:b])
+    return total
+
+
+@pytest.mark.parametrize("prefix,items", [
+    ([64], [[9, 9, 9, 9]]),
+    ([0, 37, 5], [[4, 1], [12, 3, 7], []]),
+    ([130, 1], [[1] * 20, [2, 2]]),
+])
+def test_bench_pairs_equal_the_mask(prefix, items):
+    wl = workloads.from_lengths("pairs", prefix, items, hq=4, hkv=2, d=64)
+    assert bench.visible_pairs(wl) == _mask_pairs(wl)
+
+
+def test_tiny_workload_pairs_and_flops():
+    wl = workloads.config(1)
+    assert bench.visible_pairs(wl) == _mask_pairs(wl)
+    assert bench.attention_flops(wl) == 4 * wl.d * wl.hq * _mask_pairs(wl)
+
+
+def test_single_request_workload_figures():
+    # prefix 2048 + 64 items of 33 tokens, 16 query heads of 128 dims
+    wl = workloads.config(2)
+    lq, s, n = 2048, 33, 64
+    pairs = lq * (lq + 1) // 2 + n * (s * lq + s * (s + 1) // 2)
+    assert pairs == 6_459_456
+    assert bench.visible_pairs(wl) == pairs
+    assert bench.attention_flops(wl) == 4 * 128 * 16 * pairs == 52_915_863_552
