@@ -45,3 +45,12 @@ def test_single_request_workload_figures():
     assert pairs == 6_459_456
     assert bench.visible_pairs(wl) == pairs
     assert bench.attention_flops(wl) == 4 * 128 * 16 * pairs == 52_915_863_552
+
+
+def test_single_request_scoring_figures():
+    # 64 items, H = 1024, V = 151936, K = 2: FLOPs 2NHV; bytes: the LM head and
+    # the readout rows read once (bf16), the label log-probs written (fp32)
+    wl = workloads.config(2)
+    flops, nbytes = bench.lm_head_cost(wl)
+    assert flops == 2 * 64 * 1024 * 151936 == 19_914_555_392
+    assert nbytes == 2 * (151936 * 1024 + 64 * 1024) + 4 * 64 * 2 == 311_296_512
