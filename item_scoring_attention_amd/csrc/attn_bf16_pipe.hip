@@ -64,49 +64,54 @@ static_assert(BM == 64 && BN == 64, "the loop block is written for 64 x 64 tiles
 struct LoopArgs {
   uint32_t ka[8];   // LDS byte address of this lane's K fragment slot, per 16-dim step
   uint32_t va[4];   // LDS byte address of this lane's V^T read, per 32-dim block
-  uint32_t ko[4];   // global byte offset of this lane's K chunk in a tile, per DMA row group
-  uint32_t vo;      // same for V (its swizzle does not depend on the row group)
+  uint32_t ko[8];   // byte offset of this lane's K chunk in a tile, per LDS-direct load of the wave
+  uint32_t vo[8];   // same for V
   int rjt[2];       // last visible key of the lane's two query rows, minus 4g
   int rjb[2];       // first key of the rows' own item (0 for prefix rows), minus 4g
   int rlq;          // prefix length minus 4g
   int nvis, a_end, b_start, a_full;
   uint32_t kb_lo, kb_hi, vb_lo, vb_hi;  // this KV head's K and V at the request start
-  uint32_t rb64, rb4, nrec;             // 64 and 4 token rows in bytes; descriptor range
-  uint32_t wsoff, wlds;                 // this wave's first DMA row: global offset, LDS address
+  uint32_t rb64, nrec;                  // 64 token rows in bytes; descriptor range
+  uint32_t wlds;                        // LDS address of this wave's first DMA row
   float c;                              // softmax scale * log2(e)
 };
 
-#define MIS_ATTN_LOOP_OPERANDS                                                                                      \
+// Per-lane offsets of the LDS-direct loads: 4 or 8 loads per wave, tile and operand.
+#define MIS_ATTN_KV4                                                                                                \
+  [ko0] "v"(x.ko[0]), [ko1] "v"(x.ko[1]), [ko2] "v"(x.ko[2]), [ko3] "v"(x.ko[3]), [vo0] "v"(x.vo[0]),            \
+      [vo1] "v"(x.vo[1]), [vo2] "v"(x.vo[2]), [vo3] "v"(x.vo[3])
+#define MIS_ATTN_KV8                                                                                                \
+  MIS_ATTN_KV4, [ko4] "v"(x.ko[4]), [ko5] "v"(x.ko[5]), [ko6] "v"(x.ko[6]), [ko7] "v"(x.ko[7]),                 \
+      [vo4] "v"(x.vo[4]), [vo5] "v"(x.vo[5]), [vo6] "v"(x.vo[6]), [vo7] "v"(x.vo[7])
+
+#define MIS_ATTN_LOOP_OPERANDS(KV)                                                                                  \
   : [o0] "={a[0:31]}"(o0), [o1] "={a[32:63]}"(o1), [o2] "={a[64:95]}"(o2), [o3] "={a[96:127]}"(o3),              \
     [l0] "=v"(l0), [l1] "=v"(l1)                                                                                    \
   : [q0] "{a[128:159]}"(q0), [q1] "{a[160:191]}"(q1), [ka0] "v"(x.ka[0]), [ka1] "v"(x.ka[1]),                    \
     [ka2] "v"(x.ka[2]), [ka3] "v"(x.ka[3]), [ka4] "v"(x.ka[4]), [ka5] "v"(x.ka[5]), [ka6] "v"(x.ka[6]),            \
-    [ka7] "v"(x.ka[7]), [va0] "v"(x.va[0]), [va1] "v"(x.va[1]), [va2] "v"(x.va[2]), [va3] "v"(x.va[3]),            \
-    [ko0] "v"(x.ko[0]), [ko1] "v"(x.ko[1]), [ko2] "v"(x.ko[2]), [ko3] "v"(x.ko[3]), [vo] "v"(x.vo),                \
+    [ka7] "v"(x.ka[7]), [va0] "v"(x.va[0]), [va1] "v"(x.va[1]), [va2] "v"(x.va[2]), [va3] "v"(x.va[3]), KV,        \
     [rjt0] "v"(x.rjt[0]), [rjt1] "v"(x.rjt[1]), [rjb0] "v"(x.rjb[0]), [rjb1] "v"(x.rjb[1]), [rlq] "v"(x.rlq),     \
     [nvis] "s"(x.nvis), [a_end] "s"(x.a_end), [b_start] "s"(x.b_start), [a_full] "s"(x.a_full),                   \
     [kb_lo] "s"(x.kb_lo), [kb_hi] "s"(x.kb_hi), [vb_lo] "s"(x.vb_lo), [vb_hi] "s"(x.vb_hi), [rb64] "s"(x.rb64),    \
-    [rb4] "s"(x.rb4), [nrec] "s"(x.nrec), [wsoff] "s"(x.wsoff), [wlds] "s"(x.wlds), [c] "s"(x.c)                  \
+    [nrec] "s"(x.nrec), [wlds] "s"(x.wlds), [c] "s"(x.c)                                                          \
   : MIS_ATTN_LOOP_CLOBBERS
 
 #define MIS_ATTN_LOOP_OPERANDS_QB1                                                                                  \
   : [o0] "={a[0:31]}"(o0), [o1] "={a[32:63]}"(o1), [l0] "=v"(l0)                                                   \
   : [q0] "{a[64:95]}"(q0), [ka0] "v"(x.ka[0]), [ka1] "v"(x.ka[1]), [ka2] "v"(x.ka[2]), [ka3] "v"(x.ka[3]),         \
     [ka4] "v"(x.ka[4]), [ka5] "v"(x.ka[5]), [ka6] "v"(x.ka[6]), [ka7] "v"(x.ka[7]), [va0] "v"(x.va[0]),            \
-    [va1] "v"(x.va[1]), [va2] "v"(x.va[2]), [va3] "v"(x.va[3]), [ko0] "v"(x.ko[0]), [ko1] "v"(x.ko[1]),            \
-    [ko2] "v"(x.ko[2]), [ko3] "v"(x.ko[3]), [vo] "v"(x.vo), [rjt0] "v"(x.rjt[0]), [rjb0] "v"(x.rjb[0]),            \
-    [rlq] "v"(x.rlq), [nvis] "s"(x.nvis), [a_end] "s"(x.a_end), [b_start] "s"(x.b_start), [a_full] "s"(x.a_full), \
-    [kb_lo] "s"(x.kb_lo), [kb_hi] "s"(x.kb_hi), [vb_lo] "s"(x.vb_lo), [vb_hi] "s"(x.vb_hi), [rb64] "s"(x.rb64),    \
-    [rb4] "s"(x.rb4), [nrec] "s"(x.nrec), [wsoff] "s"(x.wsoff), [wlds] "s"(x.wlds), [c] "s"(x.c)                  \
+    [va1] "v"(x.va[1]), [va2] "v"(x.va[2]), [va3] "v"(x.va[3]), MIS_ATTN_KV4, [rjt0] "v"(x.rjt[0]),               \
+    [rjb0] "v"(x.rjb[0]), [rlq] "v"(x.rlq), [nvis] "s"(x.nvis), [a_end] "s"(x.a_end), [b_start] "s"(x.b_start),   \
+    [a_full] "s"(x.a_full), [kb_lo] "s"(x.kb_lo), [kb_hi] "s"(x.kb_hi), [vb_lo] "s"(x.vb_lo),                     \
+    [vb_hi] "s"(x.vb_hi), [rb64] "s"(x.rb64), [nrec] "s"(x.nrec), [wlds] "s"(x.wlds), [c] "s"(x.c)                \
   : MIS_ATTN_LOOP_CLOBBERS_QB1
 
 // The ring's first loads (a block of their own, issued with the kernel's own
 // loads); the loop block then finds them landed.
-#define MIS_ATTN_PROLOGUE_OPERANDS                                                                                  \
-  ::[ko0] "v"(x.ko[0]), [ko1] "v"(x.ko[1]), [ko2] "v"(x.ko[2]), [ko3] "v"(x.ko[3]), [vo] "v"(x.vo),               \
-    [nvis] "s"(x.nvis), [a_end] "s"(x.a_end), [b_start] "s"(x.b_start), [kb_lo] "s"(x.kb_lo), [kb_hi] "s"(x.kb_hi), \
-    [vb_lo] "s"(x.vb_lo), [vb_hi] "s"(x.vb_hi), [rb64] "s"(x.rb64), [rb4] "s"(x.rb4), [nrec] "s"(x.nrec),        \
-    [wsoff] "s"(x.wsoff), [wlds] "s"(x.wlds)                                                                      \
+#define MIS_ATTN_PROLOGUE_OPERANDS(KV)                                                                              \
+  ::KV, [nvis] "s"(x.nvis), [a_end] "s"(x.a_end), [b_start] "s"(x.b_start), [kb_lo] "s"(x.kb_lo),                 \
+    [kb_hi] "s"(x.kb_hi), [vb_lo] "s"(x.vb_lo), [vb_hi] "s"(x.vb_hi), [rb64] "s"(x.rb64), [nrec] "s"(x.nrec),     \
+    [wlds] "s"(x.wlds)                                                                                            \
   : MIS_ATTN_PROLOGUE_CLOBBERS
 
 // Runs the whole key-tile loop; O^T (unnormalised) and the row sums of the
@@ -121,9 +126,9 @@ __device__ __forceinline__ void attn_loop(const LoopArgs &x, const f32x32 &q0, c
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
   if constexpr (DPW == 4)
-    asm volatile(MIS_ATTN_LOOP_TEXT_DPW4 MIS_ATTN_LOOP_OPERANDS);
+    asm volatile(MIS_ATTN_LOOP_TEXT_DPW4 MIS_ATTN_LOOP_OPERANDS(MIS_ATTN_KV4));
   else
-    asm volatile(MIS_ATTN_LOOP_TEXT_DPW8 MIS_ATTN_LOOP_OPERANDS);
+    asm volatile(MIS_ATTN_LOOP_TEXT_DPW8 MIS_ATTN_LOOP_OPERANDS(MIS_ATTN_KV8));
 #pragma clang diagnostic pop
 }
 
@@ -227,13 +232,20 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
   }
   // LDS-direct loads: instruction i of a wave covers tile rows ROWS_PER_WAVE *
   // wave + 4 i + lane / 16, LDS slot lane % 16, so the lane fetches global
-  // chunk slot ^ swizzle(row); ROWS_PER_WAVE is a multiple of 16, so the K
-  // swizzle depends on i % 4 and lane / 16 only.
+  // chunk slot ^ swizzle(row) (ROWS_PER_WAVE is a multiple of 16, so the K
+  // swizzle depends on i % 4 and lane / 16 only). The whole offset of the
+  // row inside the tile sits in the per-lane offset: the buffer range check
+  // covers that offset but not the scalar one, and rows past the request's
+  // end must fail it.
+  const uint32_t wrow = uint32_t(ROWS_PER_WAVE * wave);
   {
     const int rl = lane >> 4, slot = lane & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x.ko[i] = uint32_t(rl) * kv_row_bytes + 16u * uint32_t(slot ^ ((4 * i + rl) & 15));
-    x.vo = uint32_t(rl) * kv_row_bytes + 16u * uint32_t(slot ^ (4 * (rl & 3)));
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t row = wrow + uint32_t(4 * i + rl);
+      x.ko[i] = row * kv_row_bytes + 16u * uint32_t(slot ^ ((4 * i + rl) & 15));
+      x.vo[i] = row * kv_row_bytes + 16u * uint32_t(slot ^ (4 * (rl & 3)));
+    }
   }
   const uint64_t kb = reinterpret_cast<uint64_t>(k + int64_t(base) * kv_stride + int64_t(kvh) * D);
   const uint64_t vb = reinterpret_cast<uint64_t>(v + int64_t(base) * kv_stride + int64_t(kvh) * D);
@@ -242,12 +254,9 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
   x.vb_lo = uint32_t(vb);
   x.vb_hi = uint32_t(vb >> 32);
   x.rb64 = 64u * kv_row_bytes;
-  x.rb4 = 4u * kv_row_bytes;
   // A tile descriptor starting at key k0 covers nrec - k0 * row bytes: up to
   // this head's last key of the request, so rows past the end read nothing.
   x.nrec = uint32_t(Tr) * kv_row_bytes - uint32_t(kvh) * D * 2u;
-  const uint32_t wrow = uint32_t(ROWS_PER_WAVE * wave);
-  x.wsoff = wrow * kv_row_bytes;
   x.wlds = lds0 + wrow * 256u;
   x.c = c;
   x.rlq = lq - 4 * g;
@@ -288,11 +297,11 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
   if constexpr (QB == 1)
-    asm volatile(MIS_ATTN_PROLOGUE_TEXT_QB1 MIS_ATTN_PROLOGUE_OPERANDS);
+    asm volatile(MIS_ATTN_PROLOGUE_TEXT_QB1 MIS_ATTN_PROLOGUE_OPERANDS(MIS_ATTN_KV4));
   else if constexpr (BN / HP / 4 == 4)
-    asm volatile(MIS_ATTN_PROLOGUE_TEXT_DPW4 MIS_ATTN_PROLOGUE_OPERANDS);
+    asm volatile(MIS_ATTN_PROLOGUE_TEXT_DPW4 MIS_ATTN_PROLOGUE_OPERANDS(MIS_ATTN_KV4));
   else
-    asm volatile(MIS_ATTN_PROLOGUE_TEXT_DPW8 MIS_ATTN_PROLOGUE_OPERANDS);
+    asm volatile(MIS_ATTN_PROLOGUE_TEXT_DPW8 MIS_ATTN_PROLOGUE_OPERANDS(MIS_ATTN_KV8));
 #pragma clang diagnostic pop
 
   // Visits before a_full are fully visible tiles (class 2) that end inside

@@ -111,12 +111,10 @@ S_SK = 54
 S_KEY0 = 55
 S_M2 = 56     # s[56:57] compare mask
 S_M3 = 58     # s[58:59]
-S_SO = 60     # soffset of a DMA instruction
 S_OFF = 61
 S_NV1 = 62    # scratch
 S_LAST = 63
 S_VRSRC = 64  # V buffer descriptor s[64:67]
-S_VSO = 68    # soffset of a V load
 SGPRS = list(range(40, 72))
 
 MFMA = "v_mfma_f32_32x32x16_bf16"
@@ -393,14 +391,19 @@ def dma_setup(b: Block, vis_add: int, is_k: bool, rsrc: int):
     b.emit(f"s_mov_b32 {sr(rsrc + 3)}, 0x20000")
 
 
-def dma_groups(is_k: bool, rsrc: int, so: int, lds_byte: int, dpw: int) -> list[list[str]]:
-    """The LDS-direct loads of one tile (this wave's rows), one group per load."""
+def dma_groups(is_k: bool, rsrc: int, lds_byte: int, dpw: int) -> list[list[str]]:
+    """The LDS-direct loads of one tile (this wave's rows), one group per load.
+
+    Load i's per-lane VGPR offset (ko{i} / vo{i}) holds the whole byte offset
+    of the lane's chunk inside the tile, wave row and row group included, and
+    the SGPR offset is 0: the buffer range check covers the VGPR offset (plus
+    the instruction offset) but not the SGPR offset, so rows past the
+    request's end must show in the VGPR offset to read as nothing."""
     groups = []
     for i in range(dpw):
         g = [f"s_add_u32 m0, %[wlds], {lds_byte + 1024 * i}"]
-        g.append(f"s_add_u32 {sr(so)}, {sr(so)}, %[rb4]" if i else f"s_mov_b32 {sr(so)}, %[wsoff]")
-        voff = f"%[ko{i % 4}]" if is_k else "%[vo]"
-        g.append(f"buffer_load_dwordx4 {voff}, {sr(rsrc, 4)}, {sr(so)} offen lds")
+        voff = f"%[ko{i}]" if is_k else f"%[vo{i}]"
+        g.append(f"buffer_load_dwordx4 {voff}, {sr(rsrc, 4)}, 0 offen lds")
         groups.append(g)
     return groups
 
@@ -415,8 +418,8 @@ def barrier_dma(b: Block, tp: int, dpw: int, stages: int) -> list[list[str]]:
     b.emit("s_barrier")
     dma_setup(b, tp + stages, True, S_RSRC)
     dma_setup(b, tp + stages - 1, False, S_VRSRC)
-    return (dma_groups(True, S_RSRC, S_SO, k_off(tp), dpw) +
-            dma_groups(False, S_VRSRC, S_VSO, v_lds((tp - 1) % stages, stages), dpw))
+    return (dma_groups(True, S_RSRC, k_off(tp), dpw) +
+            dma_groups(False, S_VRSRC, v_lds((tp - 1) % stages, stages), dpw))
 
 
 def pv_tail(b: Block, p_prev: int, voff: int):
@@ -565,10 +568,10 @@ def prologue_block(dpw: int, stages: int) -> list[str]:
     b = Block()
     b.emit(f"s_mov_b32 {sr(S_T)}, 0")
     for v, is_k in prologue_order(stages):
-        rsrc, so = (S_RSRC, S_SO) if is_k else (S_VRSRC, S_VSO)
+        rsrc = S_RSRC if is_k else S_VRSRC
         dma_setup(b, v, is_k, rsrc)
         lds = k_off(v) if is_k else v_lds(v, stages)
-        for g in dma_groups(is_k, rsrc, so, lds, dpw):
+        for g in dma_groups(is_k, rsrc, lds, dpw):
             for ln in g:
                 b.emit(ln)
     return [ln for ln in b.lines if ln]

@@ -44,7 +44,9 @@ softmax row is still computed whole and independently.
 """
 from __future__ import annotations
 
+import concurrent.futures as _cf
 import math
+import os
 from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
@@ -189,6 +191,35 @@ def _softmax_rows(s: np.ndarray) -> np.ndarray:
     return p / p.sum(axis=1, keepdims=True)
 
 
+def _workers(workers: Optional[int]) -> int:
+    """Worker threads for the per-head loop: the host cores this process may
+    use (at most 16), or ``workers`` when given."""
+    if workers:
+        return max(1, int(workers))
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux hosts
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _for_each(fn, items, workers: int) -> None:
+    """Run ``fn(i)`` for every item, on ``workers`` threads with BLAS held to
+    one thread each (numpy's element-wise passes release the interpreter
+    lock, so heads run side by side; each head's arithmetic is unchanged)."""
+    items = list(items)
+    if workers <= 1 or len(items) <= 1:
+        for i in items:
+            fn(i)
+        return
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1, user_api="blas"):
+        with _cf.ThreadPoolExecutor(min(workers, len(items))) as ex:
+            for f in [ex.submit(fn, i) for i in items]:
+                f.result()
+
+
 def attention(
     q: np.ndarray,
     k: np.ndarray,
@@ -198,22 +229,25 @@ def attention(
     *,
     scale: Optional[float] = None,
     rows: Optional[np.ndarray] = None,
-    row_block: int = 1024,
+    row_block: int = 256,
+    workers: Optional[int] = None,
 ) -> np.ndarray:
     """MIS attention output in fp64.
 
     ``q`` is ``[T, Hq, D]``, ``k``/``v`` are ``[T, Hkv, D]`` (bf16 bits or
     floats). Returns ``[T, Hq, D]``, or ``[len(rows), Hq, D]`` for the packed
     query indices in ``rows`` when given. Every output row is the full softmax
-    over all keys of its request with the Eq. 4 mask added.
+    over all keys of its request with the Eq. 4 mask added. Heads are
+    independent and run on ``workers`` threads (default: the host's cores, at
+    most 16).
     """
-    qf, kf, vf = as_f64(q), as_f64(k), as_f64(v)
-    T, hq, d = qf.shape
-    hkv = kf.shape[1]
+    T, hq, d = q.shape
+    hkv = k.shape[1]
     if hq % hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     if scale is None or scale <= 0:
         scale = 1.0 / math.sqrt(d)
+    nw = _workers(workers)
     want = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.zeros((want.shape[0], hq, d))
     req_of = np.searchsorted(np.asarray(cu_seqlens[1:]), want, side="right")
@@ -222,13 +256,19 @@ def attention(
         sel = np.nonzero(req_of == r)[0]
         local = want[sel] - a
         ids = item_id[a:b]
+        kf, vf = as_f64(k[a:b]), as_f64(v[a:b])
         for c0 in range(0, local.shape[0], row_block):
             lrows = local[c0 : c0 + row_block]
+            dst = sel[c0 : c0 + row_block]
             m = mask_rows(ids, lrows)
-            for h in range(hq):
+            qf = as_f64(q[a + lrows])
+
+            def head(h, qf=qf, m=m, dst=dst):
                 g = (h * hkv) // hq
-                s = scale * (qf[a + lrows, h, :] @ kf[a:b, g, :].T) + m
-                out[sel[c0 : c0 + row_block], h, :] = _softmax_rows(s) @ vf[a:b, g, :]
+                s = scale * (qf[:, h, :] @ kf[:, g, :].T) + m
+                out[dst, h, :] = _softmax_rows(s) @ vf[:, g, :]
+
+            _for_each(head, range(hq), nw)
     return out
 
 

@@ -11,7 +11,7 @@ import torch
 import item_scoring_attention_amd as mis
 import oracle
 import workloads
-from gpu_common import TOL_BF16_ATTN, TOL_F32, build, dev, host, say, segments_oracle
+from gpu_common import TOL_BF16_ATTN, TOL_F32, build, dev, host, nan_like, say, segments_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def _item_mask(wl):
 def _append(wl, q, k, v):
     seg = build(wl)
     qd, kd, vd = dev(q), dev(k), dev(v)
-    o = torch.full_like(qd, float("nan"))
+    o = nan_like(qd)
     mis.mis_attention_append(seg, qd, kd, vd, o)
     torch.cuda.synchronize()
     return seg, qd, kd, vd, o
@@ -68,7 +68,7 @@ def test_append_equals_prefill_item_rows_bit_for_bit_single_request_workload():
     say(f"[append] {wl.name}")
     q, k, v = workloads.qkv(wl)
     seg, qd, kd, vd, o = _append(wl, q, k, v)
-    full = host(mis.mis_attention_prefill(seg, qd, kd, vd))
+    full = host(mis.mis_attention_prefill(seg, qd, kd, vd, o=nan_like(qd)))
     items, _ = _item_mask(wl)
     assert np.array_equal(host(o)[items], full[items])
 
@@ -80,6 +80,6 @@ def test_append_equals_prefill_item_rows_bit_for_bit_long_visit_lists():
     say(f"[append] {wl.name} T={wl.total_tokens}")
     q, k, v = workloads.qkv(wl)
     seg, qd, kd, vd, o = _append(wl, q, k, v)
-    full = host(mis.mis_attention_prefill(seg, qd, kd, vd))
+    full = host(mis.mis_attention_prefill(seg, qd, kd, vd, o=nan_like(qd)))
     items, _ = _item_mask(wl)
     assert np.array_equal(host(o)[items], full[items])

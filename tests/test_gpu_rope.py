@@ -13,7 +13,7 @@ import torch
 import item_scoring_attention_amd as mis
 import oracle
 import workloads
-from gpu_common import TOL_BF16_ATTN, TOL_F32, build, dev, host, say, segments_oracle
+from gpu_common import TOL_BF16_ATTN, TOL_F32, build, dev, host, nan_like, say, segments_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -89,7 +89,7 @@ def test_mis_with_rope_equals_single_item_scoring(dtype, d, tol):
     seg = build(wl)
     qd, kd = dev(q), dev(k)
     mis.mis_apply_rope(seg, qd, kd, 1e4)
-    o = host(mis.mis_attention_prefill(seg, qd, kd, dev(v)))
+    o = host(mis.mis_attention_prefill(seg, qd, kd, dev(v), o=nan_like(qd)))
     torch.cuda.synchronize()
     sis = oracle.sis_rope_attention(q, k, v, wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, 1e4)
     assert np.abs(oracle.as_f64(o) - sis).max() <= tol
