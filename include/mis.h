@@ -230,6 +230,34 @@ int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden
                      size_t ws_bytes, void *stream);
 
 /*
+ * Bytes of the scoring workspace the library keeps on each GPU for
+ * mis_score_labels_noalloc (16 MiB: the partials of about 1,700 items at a
+ * 152K-token vocabulary, 2,000 at 128K).
+ */
+#define MIS_SCORE_SCRATCH_BYTES (16u << 20)
+
+/*
+ * mis_score_labels without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). It computes exactly what
+ * mis_score_labels computes, with the same kernels, and keeps the per-tile
+ * partials in a device array of MIS_SCORE_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; it calls no device
+ * or host allocator. Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller. Nothing in the array needs clearing between
+ * calls (each call writes every partial it reads).
+ *
+ * Arguments as for mis_score_labels, without ws/ws_bytes. Errors: those of
+ * mis_score_labels, and WORKSPACE when the call's partials (2 * N *
+ * ceil(V/128) + N * K floats, each part rounded up to 256 bytes) exceed
+ * MIS_SCORE_SCRATCH_BYTES.
+ */
+int mis_score_labels_noalloc(const mis_segments *seg, const void *hidden, int32_t hidden_size,
+                             const void *lm_head, int32_t vocab, mis_dtype dt, const int32_t *label_ids_h,
+                             int32_t num_labels, int32_t apply_softmax, float *scores, void *stream);
+
+/*
  * Label scores at caller-chosen token rows: one row of K label scores for
  * each entry of positions_h, from hidden[positions_h[r]], computed exactly as
  * in mis_score_labels. This serves several readout markers per item (setwise

@@ -10,7 +10,9 @@ The computation lives in ``libmis.so`` (HIP kernels behind the C ABI of
   ``mis_attention_append``: the same for item rows only, against a cached prefix;
 * ``mis_score_labels``: readout gather, LM-head contraction and full-vocab
   logsumexp, writing one label-score row per item (``mis_score_labels_at``:
-  at any token rows, e.g. several readout markers per item).
+  at any token rows, e.g. several readout markers per item;
+  ``mis_score_labels_noalloc``: with the library's own per-GPU scratch, for
+  callers that cannot allocate).
 
 ``pack_requests`` (host only) turns queries, candidate items and a delimiter
 token into the packed token ids and the offsets ``mis_build_segments`` takes.
@@ -26,6 +28,7 @@ from ._lib import (  # noqa: F401
     MIS_ERR_WORKSPACE,
     MIS_F32,
     MIS_MAX_LABELS,
+    MIS_SCORE_SCRATCH_BYTES,
     MIS_OK,
     MisError,
     MisSegments,
@@ -41,6 +44,7 @@ from ._lib import (  # noqa: F401
     mis_build_segments,
     mis_score_labels,
     mis_score_labels_at,
+    mis_score_labels_noalloc,
     mis_score_workspace_bytes,
     mis_segments_bytes,
     version,

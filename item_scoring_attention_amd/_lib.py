@@ -25,6 +25,7 @@ MIS_ERR_WORKSPACE = -4
 MIS_ERR_UNSUPPORTED = -5
 MIS_ERR_HIP = -6
 MIS_MAX_LABELS = 256
+MIS_SCORE_SCRATCH_BYTES = 16 << 20
 
 MIS_F32 = 0
 MIS_BF16 = 1
@@ -95,6 +96,10 @@ SIGNATURES = {
                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_int, _i32p,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mis_score_labels_noalloc": (ctypes.c_int, [ctypes.POINTER(MisSegments), ctypes.c_void_p, ctypes.c_int32,
+                                                ctypes.c_void_p, ctypes.c_int32, ctypes.c_int, _i32p,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                                ctypes.c_void_p]),
     "mis_score_labels_at": (ctypes.c_int, [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int,
                                            _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -364,6 +369,31 @@ def mis_score_labels(seg: Segments, hidden, lm_head, label_ids: Sequence[int],
                                    _ptr_i32(lab), K, 1 if apply_softmax else 0,
                                    _dev(scores, "scores"), _dev(ws, "ws"),
                                    ws.numel() * ws.element_size(), _stream(stream)))
+    return scores
+
+
+def mis_score_labels_noalloc(seg: Segments, hidden, lm_head, label_ids: Sequence[int],
+                             apply_softmax: bool = False, scores=None, stream=None):
+    """``mis_score_labels`` with the library's own per-GPU scratch instead of a
+    workspace (the C call allocates nothing; pass ``scores`` to allocate
+    nothing here either). Calls that overlap on one GPU race."""
+    torch = _torch()
+    if hidden.dim() != 2 or lm_head.dim() != 2 or hidden.shape[1] != lm_head.shape[1]:
+        raise ValueError("hidden must be [T, H] and lm_head [V, H]")
+    if hidden.shape[0] != seg.total_tokens:
+        raise ValueError("hidden rows differ from the segments' token count")
+    if hidden.dtype != lm_head.dtype:
+        raise ValueError("hidden and lm_head dtypes differ")
+    lab = _host_i32(label_ids)
+    N, K = seg.total_items, len(lab)
+    if scores is None:
+        scores = torch.empty((N, K), dtype=torch.float32, device=hidden.device)
+    elif scores.dtype != torch.float32 or tuple(scores.shape) != (N, K):
+        raise ValueError("scores must be float32 [N, K]")
+    _check(load().mis_score_labels_noalloc(ctypes.byref(seg.struct), _dev(hidden, "hidden"), hidden.shape[1],
+                                           _dev(lm_head, "lm_head"), lm_head.shape[0], _dtype_code(hidden),
+                                           _ptr_i32(lab), K, 1 if apply_softmax else 0, _dev(scores, "scores"),
+                                           _stream(stream)))
     return scores
 
 

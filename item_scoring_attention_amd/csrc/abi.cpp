@@ -452,28 +452,36 @@ int mis_score_workspace_bytes(int32_t num_items, int32_t vocab, int32_t num_labe
   return ok();
 }
 
-int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden_size,
-                     const void *lm_head, int32_t vocab, mis_dtype dt, const int32_t *label_ids_h,
-                     int32_t num_labels, int32_t apply_softmax, float *scores, void *ws,
-                     size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of mis_score_labels and mis_score_labels_noalloc (all on
+// the host); *need = workspace bytes of the call.
+int score_labels_check(const mis_segments *seg, const void *hidden, int32_t hidden_size, const void *lm_head,
+                       int32_t vocab, mis_dtype dt, const int32_t *label_ids_h, int32_t num_labels,
+                       const float *scores, size_t *need) {
   if (!seg) return fail(MIS_ERR_ARG, "seg is NULL");
-  if (!hidden || !lm_head || !ws) return fail(MIS_ERR_ARG, "hidden, lm_head and ws must be non-NULL");
+  if (!hidden || !lm_head) return fail(MIS_ERR_ARG, "hidden and lm_head must be non-NULL");
   if (!scores && seg->total_items > 0) return fail(MIS_ERR_ARG, "scores is NULL");
   if (!label_ids_h) return fail(MIS_ERR_ARG, "label_ids is NULL");
-  size_t need;
-  int rc = mis_score_workspace_bytes(seg->total_items, vocab, num_labels, hidden_size, dt, &need);
+  int rc = mis_score_workspace_bytes(seg->total_items, vocab, num_labels, hidden_size, dt, need);
   if (rc) return rc;
   for (int32_t i = 0; i < num_labels; ++i)
     if (label_ids_h[i] < 0 || label_ids_h[i] >= vocab)
       return fail(MIS_ERR_LABEL, "label id %d at position %d outside [0, %d)", label_ids_h[i], i, vocab);
-  if (ws_bytes < need) return fail(MIS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, need);
   if (dt == MIS_BF16 && hidden_size % 32)
     return fail(MIS_ERR_UNSUPPORTED, "bf16 scoring needs hidden_size %% 32 == 0 (got %d)", hidden_size);
   // a vocabulary tile's LM-head rows are addressed with 32-bit byte offsets
   if (hidden_size > (1 << 22))
     return fail(MIS_ERR_UNSUPPORTED, "hidden_size %d is above the 4194304 the scoring kernels address", hidden_size);
-  if (seg->total_items == 0) return ok();
-  if (!seg->readout_pos) return fail(MIS_ERR_ARG, "seg is not a built segment descriptor");
+  if (seg->total_items > 0 && !seg->readout_pos) return fail(MIS_ERR_ARG, "seg is not a built segment descriptor");
+  return MIS_OK;
+}
+
+int score_labels_launch(const mis_segments *seg, const void *hidden, int32_t hidden_size, const void *lm_head,
+                        int32_t vocab, mis_dtype dt, const int32_t *label_ids_h, int32_t num_labels,
+                        int32_t apply_softmax, float *scores, void *ws, void *stream) {
   mis::LabelArgs la{};
   la.k = num_labels;
   std::memcpy(la.ids, label_ids_h, sizeof(int32_t) * num_labels);
@@ -482,6 +490,47 @@ int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden
                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "scoring launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mis_score_labels(const mis_segments *seg, const void *hidden, int32_t hidden_size,
+                     const void *lm_head, int32_t vocab, mis_dtype dt, const int32_t *label_ids_h,
+                     int32_t num_labels, int32_t apply_softmax, float *scores, void *ws,
+                     size_t ws_bytes, void *stream) {
+  size_t need;
+  int rc = score_labels_check(seg, hidden, hidden_size, lm_head, vocab, dt, label_ids_h, num_labels, scores, &need);
+  if (rc) return rc;
+  if (!ws) return fail(MIS_ERR_ARG, "ws is NULL");
+  if (ws_bytes < need) return fail(MIS_ERR_WORKSPACE, "ws_bytes %zu < required %zu", ws_bytes, need);
+  if (seg->total_items == 0) return ok();
+  return score_labels_launch(seg, hidden, hidden_size, lm_head, vocab, dt, label_ids_h, num_labels, apply_softmax,
+                             scores, ws, stream);
+}
+
+int mis_score_labels_noalloc(const mis_segments *seg, const void *hidden, int32_t hidden_size,
+                             const void *lm_head, int32_t vocab, mis_dtype dt, const int32_t *label_ids_h,
+                             int32_t num_labels, int32_t apply_softmax, float *scores, void *stream) {
+  size_t need;
+  int rc = score_labels_check(seg, hidden, hidden_size, lm_head, vocab, dt, label_ids_h, num_labels, scores, &need);
+  if (rc) return rc;
+  // the partials and label logits only (the readout-position region of the
+  // workspace serves mis_score_labels_at)
+  const size_t nvt = size_t(mis::score_vocab_tiles(vocab));
+  const size_t used = score_ws_positions_offset(size_t(std::max(seg->total_items, 1)), nvt, num_labels);
+  if (used > size_t(MIS_SCORE_SCRATCH_BYTES))
+    return fail(MIS_ERR_WORKSPACE,
+                "%d items x %d vocabulary rows x %d labels need %zu bytes of scratch; the library's scratch holds "
+                "%zu (mis_score_labels takes a caller workspace of any size)",
+                seg->total_items, vocab, num_labels, used, size_t(MIS_SCORE_SCRATCH_BYTES));
+  if (seg->total_items == 0) return ok();
+  void *ws = nullptr;
+  hipError_t e = mis::score_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "device address of the scoring scratch");
+  return score_labels_launch(seg, hidden, hidden_size, lm_head, vocab, dt, label_ids_h, num_labels, apply_softmax,
+                             scores, ws, stream);
 }
 
 int mis_score_labels_at(const int32_t *positions_h, int32_t num_rows, int32_t num_tokens,

@@ -80,6 +80,11 @@ hipError_t launch_rope(const mis_segments &seg, void *q, void *k, mis_dtype dt, 
 // positions (used by mis_score_labels_at).
 inline int score_vocab_tiles(int vocab) { return (vocab + kScoreBlockV - 1) / kScoreBlockV; }
 
+// Device address, on the current device, of the library's own scoring
+// workspace (MIS_SCORE_SCRATCH_BYTES, a static device array in score.hip);
+// looked up once per device and kept. Allocates nothing.
+hipError_t score_scratch(void **ptr);
+
 // N rows of label scores from the hidden rows at readout_pos[0 .. N-1].
 hipError_t launch_score(const int32_t *readout_pos, int num_rows, const void *hidden, int h, const void *lm_head,
                         int vocab, mis_dtype dt, const LabelArgs &labels, int apply_softmax,

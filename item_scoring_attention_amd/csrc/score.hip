@@ -18,6 +18,7 @@
 // softmax over the label logits).
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "gfx950_util.h"
 #include "mis_internal.h"
@@ -618,6 +619,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 }
 
 }  // namespace
+
+// The workspace of mis_score_labels_noalloc: partial maxima, partial sums
+// and label logits, as in a caller's workspace. Every GPU the library runs
+// on holds its own copy until the process ends. Host code never passes the
+// name itself to a kernel (on the host it is only a stand-in for the
+// symbol): score_scratch looks up the device address once per device.
+static __device__ __align__(256) unsigned char scratch[MIS_SCORE_SCRATCH_BYTES];
+
+hipError_t score_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_score(const int32_t *readout_pos, int N, const void *hidden, int H, const void *lm_head,
                         int V, mis_dtype dt, const LabelArgs &labels, int apply_softmax,
