@@ -278,6 +278,39 @@ int mis_score_labels_at(const int32_t *positions_h, int32_t num_rows, int32_t nu
                         mis_dtype dt, const int32_t *label_ids_h, int32_t num_labels,
                         int32_t apply_softmax, float *scores, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Kernel choice of the calling thread, for tests and A/B comparisons (every
+ * choice computes the same result). Each call picks its kernel by shape
+ * unless a choice is set here; the setting holds for later calls on the same
+ * thread until changed, and other threads are not affected.
+ *   attention: NULL, "" or "auto" (by shape); "pipe" (pipelined loop, 64 query
+ *              rows per wave); "pipe32" (pipelined loop, 32 rows per wave);
+ *              "classic" (plain loop). The pipelined loops need an even GQA
+ *              group size: odd group sizes always take the plain loop.
+ *   score:     NULL, "" or "auto"; "narrow" (128 vocabulary rows x up to 128
+ *              items per workgroup); "wide" (256 rows, item blocks by shape) or
+ *              "wide3", "wide4", "wide5", "wide6", "wide8" (that many blocks of
+ *              32 items). Applies to bf16 with hidden_size % 64 == 0.
+ * Errors: ARG (unknown name; the previous setting stays).
+ */
+int mis_set_kernel_choice(const char *attention, const char *score);
+
+/*
+ * Name of the kernel that mis_attention_prefill launches on this thread for
+ * these arguments, e.g. "attn_pipe_kernel<4, 1>" ("" and mis_last_error()
+ * set when the arguments are invalid). Static storage; never NULL.
+ */
+const char *mis_attention_kernel_name(const mis_segments *seg, mis_dtype dt, int32_t hq, int32_t hkv,
+                                      int32_t head_dim);
+
+/*
+ * Name of the LM-head kernel that mis_score_labels launches on this thread
+ * for num_items items of hidden size hidden_size, e.g.
+ * "score_wide_kernel<8, 2>" (the combine kernel always follows it). Thread-
+ * local storage, valid until the next call on this thread; never NULL.
+ */
+const char *mis_score_kernel_name(int32_t num_items, int32_t hidden_size, mis_dtype dt);
+
 /* Text of the last error on this thread ("" if none). Never NULL. */
 const char *mis_last_error(void);
 

@@ -35,6 +35,7 @@ from ._lib import (  # noqa: F401
     MisValueError,
     SIGNATURES,
     Segments,
+    attention_kernel_name,
     last_error,
     load,
     mis_apply_rope,
@@ -47,6 +48,8 @@ from ._lib import (  # noqa: F401
     mis_score_labels_noalloc,
     mis_score_workspace_bytes,
     mis_segments_bytes,
+    score_kernel_name,
+    set_kernel_choice,
     version,
 )
 from .pack import Packed, build_packed_segments, pack_requests  # noqa: F401,E402

@@ -104,6 +104,10 @@ SIGNATURES = {
                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int,
                                            _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mis_set_kernel_choice": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_char_p]),
+    "mis_attention_kernel_name": (ctypes.c_char_p, [ctypes.POINTER(MisSegments), ctypes.c_int, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_int32]),
+    "mis_score_kernel_name": (ctypes.c_char_p, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int]),
     "mis_last_error": (ctypes.c_char_p, []),
     "mis_version": (ctypes.c_char_p, []),
 }
@@ -201,6 +205,37 @@ def _dev(t, name: str):
 
 def version() -> str:
     return load().mis_version().decode()
+
+
+def set_kernel_choice(attention: Optional[str] = None, score: Optional[str] = None) -> None:
+    """Force the attention / scoring kernel variant of this thread's later
+    calls (``None`` or ``"auto"``: picked by shape); see ``include/mis.h``."""
+    enc = lambda x: None if x is None else x.encode()
+    _check(load().mis_set_kernel_choice(enc(attention), enc(score)))
+
+
+def _code(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    torch = _torch()
+    return MIS_BF16 if dtype == torch.bfloat16 else MIS_F32
+
+
+def attention_kernel_name(seg: "Segments", dtype, hq: int, hkv: int, head_dim: int) -> str:
+    """The kernel ``mis_attention_prefill`` launches on this thread for these arguments."""
+    name = load().mis_attention_kernel_name(ctypes.byref(seg.struct), _code(dtype), int(hq), int(hkv),
+                                            int(head_dim)).decode()
+    if not name:
+        raise MisValueError(MIS_ERR_ARG, last_error())
+    return name
+
+
+def score_kernel_name(num_items: int, hidden_size: int, dtype) -> str:
+    """The LM-head kernel ``mis_score_labels`` launches on this thread for this shape."""
+    name = load().mis_score_kernel_name(int(num_items), int(hidden_size), _code(dtype)).decode()
+    if not name:
+        raise MisValueError(MIS_ERR_ARG, last_error())
+    return name
 
 
 def last_error() -> str:

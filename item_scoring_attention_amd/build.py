@@ -2,7 +2,9 @@
 
 Usage: ``python -m item_scoring_attention_amd.build`` (or ``build()``). Every
 call recompiles all sources; objects go to ``_build/`` next to this file and
-the shared library to ``libmis.so`` in the package directory.
+the shared libraries to the package directory: ``libmis.so`` (the C ABI) and
+``libmis_probe.so`` (the MFMA-rate probe the benchmark prices against; not
+part of the ABI).
 """
 from __future__ import annotations
 
@@ -19,10 +21,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmis.so")
+PROBE_LIB = os.path.join(PKG, "libmis_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "segments.hip", "rope.hip", "attn_f32.hip", "attn_bf16.hip", "attn_bf16_pipe.hip",
            "score.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 # Per-source extra flags. The attention kernels keep their MFMA accumulators
 # in VGPRs: with the default heuristic the allocator parks them in AGPRs and
@@ -69,13 +73,8 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link ``libmis.so``; return its path."""
-    t0 = time.time()
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -88,9 +87,21 @@ def build(verbose: bool = False) -> str:
         bad = [ln.split()[-1] for ln in und.splitlines() if "__device_stub__" in ln]
         if bad:
             raise RuntimeError(f"undefined kernel launch stubs in {tmp}: {bad}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link ``libmis.so`` and
+    ``libmis_probe.so``; return the path of ``libmis.so``."""
+    t0 = time.time()
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} in {time.time() - t0:.1f}s", flush=True)
+        print(f"built {LIB} and {PROBE_LIB} in {time.time() - t0:.1f}s", flush=True)
     return LIB
 
 

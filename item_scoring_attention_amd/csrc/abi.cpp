@@ -16,6 +16,13 @@ namespace {
 
 thread_local std::string g_error;
 
+// Kernel variants forced by mis_set_kernel_choice on this thread (tests and
+// A/B comparisons); Auto = each call picks by shape.
+thread_local mis::AttnForce g_attn_force = mis::AttnForce::Auto;
+thread_local mis::ScoreForce g_score_force = mis::ScoreForce::Auto;
+thread_local int g_score_force_ni = 0;
+thread_local char g_kernel_name[64];
+
 int fail(int code, const char *fmt, ...) {
   char buf[512];
   va_list ap;
@@ -397,7 +404,8 @@ int attention_call(const mis_segments *seg, const void *q, const void *k, const 
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = dt == MIS_BF16
-                     ? mis::launch_attention_bf16(*seg, q, k, v, o, hq, hkv, head_dim, scale, items_only, st)
+                     ? mis::launch_attention_bf16(*seg, q, k, v, o, hq, hkv, head_dim, scale, items_only,
+                                                  mis::pick_attention_bf16(*seg, hq, hkv, g_attn_force), st)
                      : mis::launch_attention_f32(*seg, static_cast<const float *>(q),
                                                  static_cast<const float *>(k),
                                                  static_cast<const float *>(v), static_cast<float *>(o),
@@ -485,8 +493,9 @@ int score_labels_launch(const mis_segments *seg, const void *hidden, int32_t hid
   mis::LabelArgs la{};
   la.k = num_labels;
   std::memcpy(la.ids, label_ids_h, sizeof(int32_t) * num_labels);
+  const mis::ScoreKernel kern = mis::pick_score(seg->total_items, hidden_size, dt, g_score_force, g_score_force_ni);
   hipError_t e = mis::launch_score(seg->readout_pos, seg->total_items, hidden, hidden_size, lm_head, vocab, dt, la,
-                                   apply_softmax ? 1 : 0, scores, static_cast<float *>(ws),
+                                   apply_softmax ? 1 : 0, scores, static_cast<float *>(ws), kern,
                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "scoring launch");
   return ok();
@@ -566,9 +575,56 @@ int mis_score_labels_at(const int32_t *positions_h, int32_t num_rows, int32_t nu
   la.k = num_labels;
   std::memcpy(la.ids, label_ids_h, sizeof(int32_t) * num_labels);
   e = mis::launch_score(pos_dev, num_rows, hidden, hidden_size, lm_head, vocab, dt, la, apply_softmax ? 1 : 0,
-                        scores, static_cast<float *>(ws), st);
+                        scores, static_cast<float *>(ws),
+                        mis::pick_score(num_rows, hidden_size, dt, g_score_force, g_score_force_ni), st);
   if (e != hipSuccess) return hip_fail(e, "scoring launch");
   return ok();
+}
+
+int mis_set_kernel_choice(const char *attention, const char *score) {
+  mis::AttnForce af;
+  if (!attention || !*attention || !std::strcmp(attention, "auto")) af = mis::AttnForce::Auto;
+  else if (!std::strcmp(attention, "pipe")) af = mis::AttnForce::Pipe;
+  else if (!std::strcmp(attention, "pipe32")) af = mis::AttnForce::Pipe32;
+  else if (!std::strcmp(attention, "classic")) af = mis::AttnForce::Classic;
+  else return fail(MIS_ERR_ARG, "unknown attention kernel choice '%s' (auto, pipe, pipe32, classic)", attention);
+  mis::ScoreForce sf;
+  int ni = 0;
+  if (!score || !*score || !std::strcmp(score, "auto")) sf = mis::ScoreForce::Auto;
+  else if (!std::strcmp(score, "narrow")) sf = mis::ScoreForce::Narrow;
+  else if (!std::strcmp(score, "wide")) sf = mis::ScoreForce::Wide;
+  else if (!std::strncmp(score, "wide", 4) && score[4] >= '3' && score[4] <= '8' && score[4] != '7' && !score[5]) {
+    sf = mis::ScoreForce::Wide;
+    ni = score[4] - '0';
+  } else {
+    return fail(MIS_ERR_ARG, "unknown scoring kernel choice '%s' (auto, narrow, wide, wide3..wide6, wide8)", score);
+  }
+  g_attn_force = af;
+  g_score_force = sf;
+  g_score_force_ni = ni;
+  return ok();
+}
+
+const char *mis_attention_kernel_name(const mis_segments *seg, mis_dtype dt, int32_t hq, int32_t hkv,
+                                      int32_t head_dim) {
+  int32_t bm, bn;
+  if (!seg) {
+    fail(MIS_ERR_ARG, "seg is NULL");
+    return "";
+  }
+  if (mis_attention_tile_shape(dt, hq, hkv, head_dim, &bm, &bn) != MIS_OK) return "";
+  if (dt != MIS_BF16) return "attn_f32_kernel";
+  return mis::attention_bf16_name(mis::pick_attention_bf16(*seg, hq, hkv, g_attn_force));
+}
+
+const char *mis_score_kernel_name(int32_t num_items, int32_t hidden_size, mis_dtype dt) {
+  if (num_items < 0 || hidden_size < 1) {
+    fail(MIS_ERR_ARG, "need num_items >= 0 and hidden_size >= 1");
+    return "";
+  }
+  mis::score_kernel_name(mis::pick_score(num_items, hidden_size, dt, g_score_force, g_score_force_ni),
+                         g_kernel_name, sizeof(g_kernel_name));
+  return g_kernel_name;
 }
 
 }  // extern "C"

@@ -59,8 +59,6 @@
 // share it); the O rescale is skipped when no lane of the wave raised it.
 // Row sums add the bf16-rounded P (the values the PV product uses), two per
 // v_dot2_f32_bf16.
-#include <cstdlib>
-#include <cstring>
 #include <utility>
 
 #include "gfx950_util.h"
@@ -438,39 +436,56 @@ hipError_t launch_variant(const mis_segments &seg, const __bf16 *qp, const __bf1
 
 }  // namespace
 
+AttnKernel pick_attention_bf16(const mis_segments &seg, int hq, int hkv, AttnForce force) {
+  const int gsz = hq / hkv;
+  // The pipelined loops are generated for even GQA group sizes; odd ones
+  // (MHA included) always take this file's plain loop with one head.
+  if (gsz % 2 != 0) return AttnKernel::Classic1;
+  switch (force) {
+    case AttnForce::Pipe: return gsz % 4 == 0 ? AttnKernel::Pipe4 : AttnKernel::Pipe2;
+    case AttnForce::Pipe32: return AttnKernel::Pipe32;
+    case AttnForce::Classic: return AttnKernel::Classic2;
+    case AttnForce::Auto: break;
+  }
+  // Long runs of work (GQA groups of 4 or more, query tiles that visit 48
+  // key tiles or more on average, and at least 8 four-head workgroups per
+  // CU) take the pipelined loop with 64 query rows per wave: one wave per
+  // SIMD, so it cannot hide the fixed cost of starting a query tile behind
+  // another workgroup, but its loop is the fastest. Other shapes take the
+  // pipelined loop with 32 rows per wave, two waves per SIMD.
+  const bool long_runs = gsz % 4 == 0 && int64_t(seg.num_visits) >= 48 * int64_t(seg.num_work) &&
+                         int64_t(seg.num_work) * (hq / 4) >= 8 * int64_t(device_cus());
+  return long_runs ? AttnKernel::Pipe4 : AttnKernel::Pipe32;
+}
+
+const char *attention_bf16_name(AttnKernel k) {
+  switch (k) {
+    case AttnKernel::Pipe4: return "attn_pipe_kernel<4, 1>";
+    case AttnKernel::Pipe2: return "attn_pipe_kernel<2, 1>";
+    case AttnKernel::Pipe32: return "attn_pipe_kernel<2, 2>";
+    case AttnKernel::Classic2: return "attn_dma_kernel<2, 2>";
+    case AttnKernel::Classic1: return "attn_dma_kernel<2, 1>";
+  }
+  return "";
+}
+
 hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const void *k,
                                  const void *v, void *o, int hq, int hkv, int d, float scale,
-                                 int items_only, hipStream_t st) {
+                                 int items_only, AttnKernel kernel, hipStream_t st) {
   if (d != D) return hipErrorInvalidValue;
-  const int gsz = hq / hkv;
   const float c = scale * kLog2e;
   const __bf16 *qp = static_cast<const __bf16 *>(q);
   const __bf16 *kp = static_cast<const __bf16 *>(k);
   const __bf16 *vp = static_cast<const __bf16 *>(v);
   __bf16 *op = static_cast<__bf16 *>(o);
-  // Three kernels. Long runs of work (GQA groups of 4 or more, query tiles
-  // that visit 48 key tiles or more on average, and at least 8 four-head
-  // workgroups per CU) take the pipelined loop with 64 query rows per wave:
-  // one wave per SIMD, so it cannot hide the fixed cost of starting a query
-  // tile behind another workgroup, but its loop is the fastest. Other
-  // even group sizes take the pipelined loop with 32 rows per wave, two waves
-  // per SIMD (2 row blocks x 2 heads per workgroup); odd group sizes this
-  // file's kernel (2 row blocks x 1 head, plain loop, two waves per SIMD).
-  // MIS_ATTENTION_KERNEL=pipe, =pipe32 or =classic forces one (tests run
-  // every shape through each); the pipelined ones need an even group size.
-  const char *force = std::getenv("MIS_ATTENTION_KERNEL");
-  const bool want_pipe = force && std::strcmp(force, "pipe") == 0;
-  const bool want_classic = force && std::strcmp(force, "classic") == 0;
-  const bool want_pipe32 = force && std::strcmp(force, "pipe32") == 0;
-  const bool pipe_fits = gsz % 2 == 0;
-  const bool pipe_pays = gsz % 4 == 0 && int64_t(seg.num_visits) >= 48 * int64_t(seg.num_work) &&
-                         int64_t(seg.num_work) * (hq / 4) >= 8 * int64_t(device_cus());
-  if (pipe_fits && (want_pipe || (pipe_pays && !want_classic && !want_pipe32)))
-    return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, st);
-  if (pipe_fits && !want_classic)
-    return launch_attention_bf16_pipe32(seg, q, k, v, o, hq, hkv, scale, items_only, st);
-  if (gsz % 2 == 0) return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
-  return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
+  switch (kernel) {
+    case AttnKernel::Pipe4:
+    case AttnKernel::Pipe2: return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, st);
+    case AttnKernel::Pipe32: return launch_attention_bf16_pipe32(seg, q, k, v, o, hq, hkv, scale, items_only, st);
+    case AttnKernel::Classic2: return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
+    case AttnKernel::Classic1: return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace mis

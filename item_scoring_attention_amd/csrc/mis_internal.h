@@ -51,9 +51,22 @@ hipError_t launch_attention_f32(const mis_segments &seg, const float *q, const f
                                 const float *v, float *o, int hq, int hkv, int d, float scale,
                                 int items_only, hipStream_t stream);
 
+// The bf16 attention kernels and the rule that picks one per call.
+enum class AttnKernel : int {
+  Pipe4 = 0,    // attn_pipe_kernel<4, 1>: 64 query rows per wave, 4 heads per workgroup
+  Pipe2 = 1,    // attn_pipe_kernel<2, 1>: 64 query rows per wave, 2 heads per workgroup
+  Pipe32 = 2,   // attn_pipe_kernel<2, 2>: 32 query rows per wave, two waves per SIMD
+  Classic2 = 3, // attn_dma_kernel<2, 2>: plain loop, 2 heads x 2 row blocks
+  Classic1 = 4, // attn_dma_kernel<2, 1>: plain loop, 1 head x 2 row blocks (odd group sizes)
+};
+// A caller's forced choice (tests, A/B comparisons); Auto = by shape.
+enum class AttnForce : int { Auto = 0, Pipe = 1, Pipe32 = 2, Classic = 3 };
+AttnKernel pick_attention_bf16(const mis_segments &seg, int hq, int hkv, AttnForce force);
+const char *attention_bf16_name(AttnKernel k);
+
 hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const void *k,
                                  const void *v, void *o, int hq, int hkv, int d, float scale,
-                                 int items_only, hipStream_t stream);
+                                 int items_only, AttnKernel kernel, hipStream_t stream);
 
 // 64 query rows per wave, software-pipelined key-tile loop (even GQA group
 // sizes, head_dim 128); launch_attention_bf16 dispatches to it.
@@ -85,9 +98,28 @@ inline int score_vocab_tiles(int vocab) { return (vocab + kScoreBlockV - 1) / kS
 // looked up once per device and kept. Allocates nothing.
 hipError_t score_scratch(void **ptr);
 
+// The LM-head kernels and the rule that picks one per call.
+enum class ScoreKind : int {
+  Narrow = 0,  // score_lds_kernel<NI, NS>: 128 vocabulary rows x 32 NI items (NI 1, 2, 4)
+  Wide = 1,    // score_wide_kernel<NI, NS>: 256 vocabulary rows x 32 NI items (NI 3, 4, 5, 6, 8)
+  Global = 2,  // score_bf16_kernel<NI>: operands from global memory (H % 64 != 0)
+  F32 = 3,     // score_f32_kernel
+};
+struct ScoreKernel {
+  ScoreKind kind;
+  int ni;  // item blocks of 32 per workgroup tile
+};
+// A caller's forced choice: Auto, the narrow tiles, or wide tiles with
+// force_ni item blocks (0: blocks chosen by shape). Ignored where the
+// forced kernel does not apply (fp32, H % 64 != 0).
+enum class ScoreForce : int { Auto = 0, Narrow = 1, Wide = 2 };
+ScoreKernel pick_score(int num_rows, int h, mis_dtype dt, ScoreForce force, int force_ni);
+// Writes the kernel's name into buf (at most n bytes).
+void score_kernel_name(const ScoreKernel &k, char *buf, size_t n);
+
 // N rows of label scores from the hidden rows at readout_pos[0 .. N-1].
 hipError_t launch_score(const int32_t *readout_pos, int num_rows, const void *hidden, int h, const void *lm_head,
                         int vocab, mis_dtype dt, const LabelArgs &labels, int apply_softmax,
-                        float *scores, float *ws, hipStream_t stream);
+                        float *scores, float *ws, const ScoreKernel &kernel, hipStream_t stream);
 
 }  // namespace mis

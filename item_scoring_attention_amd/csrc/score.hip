@@ -16,8 +16,7 @@
 // Pass 2 (one wave per item): merge the partials exactly,
 // lse = M + log(sum_c s_c * exp(m_c - M)), and write z_label - lse (or the
 // softmax over the label logits).
-#include <cstdlib>
-#include <cstring>
+#include <cstdio>
 #include <mutex>
 
 #include "gfx950_util.h"
@@ -647,34 +646,58 @@ hipError_t score_scratch(void **ptr) {
   return hipSuccess;
 }
 
+ScoreKernel pick_score(int N, int H, mis_dtype dt, ScoreForce force, int force_ni) {
+  if (dt != MIS_BF16) return {ScoreKind::F32, 1};
+  if (H % 64 != 0) return {ScoreKind::Global, N <= 64 ? 1 : N <= 128 ? 2 : 4};
+  // Up to 64 items stream W through the narrow tiles (every LM-head row read
+  // once); more items take the wide tiles, MFMA-bound.
+  const bool wide = force == ScoreForce::Wide || (force == ScoreForce::Auto && N > 64);
+  if (!wide) return {ScoreKind::Narrow, N <= 32 ? 1 : N <= 64 ? 2 : 4};
+  int ni = force_ni;
+  if (ni != 3 && ni != 4 && ni != 5 && ni != 6 && ni != 8) {
+    // item blocks per tile: the fewest padded items, then the widest tile
+    ni = 3;
+    for (int c : {4, 5, 6, 8}) {
+      const int pc = (N + 32 * c - 1) / (32 * c) * 32 * c, pb = (N + 32 * ni - 1) / (32 * ni) * 32 * ni;
+      if (pc <= pb) ni = c;
+    }
+  }
+  return {ScoreKind::Wide, ni};
+}
+
+// LDS ring depth of each tile shape: 3 stages while W streams once (one
+// workgroup per CU for the wide tiles up to 5 item blocks), 2 when two
+// workgroups share a CU or the readout tile is large.
+static int score_stages(const ScoreKernel &k) {
+  if (k.kind == ScoreKind::Narrow) return k.ni == 4 ? 2 : 3;
+  if (k.kind == ScoreKind::Wide) return k.ni <= 5 ? 3 : 2;
+  return 0;
+}
+
+void score_kernel_name(const ScoreKernel &k, char *buf, size_t n) {
+  switch (k.kind) {
+    case ScoreKind::Narrow: snprintf(buf, n, "score_lds_kernel<%d, %d>", k.ni, score_stages(k)); return;
+    case ScoreKind::Wide: snprintf(buf, n, "score_wide_kernel<%d, %d>", k.ni, score_stages(k)); return;
+    case ScoreKind::Global: snprintf(buf, n, "score_bf16_kernel<%d>", k.ni); return;
+    case ScoreKind::F32: snprintf(buf, n, "score_f32_kernel"); return;
+  }
+  if (n) buf[0] = 0;
+}
+
 hipError_t launch_score(const int32_t *readout_pos, int N, const void *hidden, int H, const void *lm_head,
                         int V, mis_dtype dt, const LabelArgs &labels, int apply_softmax,
-                        float *scores, float *ws, hipStream_t st) {
+                        float *scores, float *ws, const ScoreKernel &kern, hipStream_t st) {
   const int nvt = score_vocab_tiles(V);
   int nvt_used = nvt;  // vocabulary tiles of the kernel that runs (the workspace fits the most)
   const size_t part = ((sizeof(float) * size_t(N) * nvt + 255) / 256) * 256;
   float *pmax = ws;
   float *psum = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + part);
   float *plab = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + 2 * part);
-  if (dt == MIS_BF16) {
-    const __bf16 *hp = static_cast<const __bf16 *>(hidden);
-    const __bf16 *wp = static_cast<const __bf16 *>(lm_head);
-    // MIS_SCORE_KERNEL=narrow or =wide (=wideNI: NI item blocks) forces a kernel
-    // (tests run every shape through both); otherwise up to 64 items stream W
-    // through the narrow tiles and more items take the wide ones.
-    const char *force = std::getenv("MIS_SCORE_KERNEL");
-    const bool want_narrow = force && std::strncmp(force, "narrow", 6) == 0;
-    const bool want_wide = force && std::strncmp(force, "wide", 4) == 0;
-    if (H % 64 == 0 && !want_narrow && (want_wide || N > 64)) {
-      // item blocks per tile: the fewest padded items, then the widest tile
-      int ni = want_wide && force[4] ? std::atoi(force + 4) : 0;
-      if (ni != 3 && ni != 4 && ni != 5 && ni != 6 && ni != 8) {
-        ni = 3;
-        for (int c : {4, 5, 6, 8}) {
-          const int pc = (N + 32 * c - 1) / (32 * c) * 32 * c, pb = (N + 32 * ni - 1) / (32 * ni) * 32 * ni;
-          if (pc <= pb) ni = c;
-        }
-      }
+  const __bf16 *hp = static_cast<const __bf16 *>(hidden);
+  const __bf16 *wp = static_cast<const __bf16 *>(lm_head);
+  const int ni = kern.ni;
+  switch (kern.kind) {
+    case ScoreKind::Wide: {
       const int nvw = (V + 255) / 256;
       const int nit = (N + 32 * ni - 1) / (32 * ni);
       const unsigned grid = unsigned((nvw + 7) / 8 * 8 * nit);
@@ -686,14 +709,14 @@ hipError_t launch_score(const int32_t *readout_pos, int N, const void *hidden, i
         case 4: MIS_WIDE(4, 3); break;
         case 5: MIS_WIDE(5, 3); break;
         case 6: MIS_WIDE(6, 2); break;
-        default: MIS_WIDE(8, 2); break;
+        case 8: MIS_WIDE(8, 2); break;
+        default: return hipErrorInvalidValue;
       }
 #undef MIS_WIDE
       nvt_used = nvw;
-    } else if (H % 64 == 0) {
-      // 32, 64 or 128 items per workgroup; a 3-deep ring while W is streamed
-      // once (N <= 64), 2-deep (2 workgroups per CU) when item tiles reuse it
-      const int ni = N <= 32 ? 1 : N <= 64 ? 2 : 4;
+      break;
+    }
+    case ScoreKind::Narrow: {
       const int nit = (N + 32 * ni - 1) / (32 * ni);
       const unsigned grid = unsigned((nvt + 7) / 8 * 8 * nit);
       if (ni == 1)
@@ -705,20 +728,24 @@ hipError_t launch_score(const int32_t *readout_pos, int N, const void *hidden, i
       else
         score_lds_kernel<4, 2><<<grid, 256, 0, st>>>(hp, wp, H, V, N, readout_pos, labels, pmax, psum,
                                                      plab, nvt, nit);
-    } else if (N <= 64) {
-      score_bf16_kernel<1><<<dim3(nvt, (N + 63) / 64), 256, 0, st>>>(
-          hp, wp, H, V, N, readout_pos, labels, pmax, psum, plab, nvt);
-    } else if (N <= 128) {
-      score_bf16_kernel<2><<<dim3(nvt, (N + 127) / 128), 256, 0, st>>>(
-          hp, wp, H, V, N, readout_pos, labels, pmax, psum, plab, nvt);
-    } else {
-      score_bf16_kernel<4><<<dim3(nvt, (N + 255) / 256), 256, 0, st>>>(
-          hp, wp, H, V, N, readout_pos, labels, pmax, psum, plab, nvt);
+      break;
     }
-  } else {
-    score_f32_kernel<<<dim3(nvt, N), BV, 0, st>>>(static_cast<const float *>(hidden),
-                                                  static_cast<const float *>(lm_head), H, V, N,
-                                                  readout_pos, labels, pmax, psum, plab, nvt);
+    case ScoreKind::Global:
+      if (ni == 1)
+        score_bf16_kernel<1><<<dim3(nvt, (N + 63) / 64), 256, 0, st>>>(hp, wp, H, V, N, readout_pos, labels,
+                                                                      pmax, psum, plab, nvt);
+      else if (ni == 2)
+        score_bf16_kernel<2><<<dim3(nvt, (N + 127) / 128), 256, 0, st>>>(hp, wp, H, V, N, readout_pos, labels,
+                                                                        pmax, psum, plab, nvt);
+      else
+        score_bf16_kernel<4><<<dim3(nvt, (N + 255) / 256), 256, 0, st>>>(hp, wp, H, V, N, readout_pos, labels,
+                                                                        pmax, psum, plab, nvt);
+      break;
+    case ScoreKind::F32:
+      score_f32_kernel<<<dim3(nvt, N), BV, 0, st>>>(static_cast<const float *>(hidden),
+                                                    static_cast<const float *>(lm_head), H, V, N, readout_pos,
+                                                    labels, pmax, psum, plab, nvt);
+      break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

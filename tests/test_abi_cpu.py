@@ -236,3 +236,62 @@ def test_score_at_argument_errors():
     assert call([5], 1, h=100) == mis.MIS_ERR_UNSUPPORTED
     assert call([5], -1) == mis.MIS_ERR_ARG
     assert call([], 0) == mis.MIS_OK  # nothing to score: validated, nothing enqueued
+
+
+def test_kernel_choice_names_and_rejects_unknown():
+    mis.set_kernel_choice()
+    with pytest.raises(ValueError, match="unknown attention kernel choice"):
+        mis.set_kernel_choice(attention="fastest")
+    with pytest.raises(ValueError, match="unknown scoring kernel choice"):
+        mis.set_kernel_choice(score="wide7")
+    bf16 = mis.MIS_BF16
+    try:
+        # scoring: the shapes of the five workloads, then forced variants
+        assert mis.score_kernel_name(64, 1024, bf16) == "score_lds_kernel<2, 3>"
+        assert mis.score_kernel_name(300, 4096, bf16) == "score_wide_kernel<5, 3>"
+        assert mis.score_kernel_name(1024, 8192, bf16) == "score_wide_kernel<8, 2>"
+        assert mis.score_kernel_name(4, 256, mis.MIS_F32) == "score_f32_kernel"
+        assert mis.score_kernel_name(200, 96, bf16) == "score_bf16_kernel<4>"
+        mis.set_kernel_choice(score="wide4")
+        assert mis.score_kernel_name(64, 1024, bf16) == "score_wide_kernel<4, 3>"
+        mis.set_kernel_choice(score="narrow")
+        assert mis.score_kernel_name(1024, 8192, bf16) == "score_lds_kernel<4, 2>"
+        assert mis.score_kernel_name(200, 96, bf16) == "score_bf16_kernel<4>"  # H % 64 != 0
+
+        # attention: picked from the segment counts (no device memory is read)
+        seg = mis.Segments(mis.MisSegments(num_requests=4, total_tokens=115712, block_m=64, block_n=64,
+                                           num_work=1808, num_visits=1808 * 259), None)
+        mis.set_kernel_choice()
+        assert mis.attention_kernel_name(seg, bf16, 64, 8, 128) == "attn_pipe_kernel<4, 1>"
+        assert mis.attention_kernel_name(seg, bf16, 16, 8, 128) == "attn_pipe_kernel<2, 2>"
+        assert mis.attention_kernel_name(seg, bf16, 12, 4, 128) == "attn_dma_kernel<2, 1>"
+        assert mis.attention_kernel_name(seg, mis.MIS_F32, 4, 4, 64) == "attn_f32_kernel"
+        short = mis.Segments(mis.MisSegments(num_requests=1, total_tokens=4160, block_m=64, block_n=64,
+                                             num_work=65, num_visits=65 * 20), None)
+        assert mis.attention_kernel_name(short, bf16, 64, 8, 128) == "attn_pipe_kernel<2, 2>"
+        mis.set_kernel_choice(attention="pipe")
+        assert mis.attention_kernel_name(short, bf16, 16, 8, 128) == "attn_pipe_kernel<2, 1>"
+        assert mis.attention_kernel_name(short, bf16, 12, 4, 128) == "attn_dma_kernel<2, 1>"
+        mis.set_kernel_choice(attention="classic")
+        assert mis.attention_kernel_name(short, bf16, 64, 8, 128) == "attn_dma_kernel<2, 2>"
+        with pytest.raises(ValueError):
+            mis.attention_kernel_name(short, bf16, 64, 8, 64)  # bf16 is built for head_dim 128
+    finally:
+        mis.set_kernel_choice()
+
+
+def test_noalloc_scoring_rejects_bad_arguments_on_the_host():
+    lib = mis.load()
+    seg = mis.MisSegments(num_requests=1, total_tokens=10, total_items=2000, block_m=64, block_n=64,
+                          readout_pos=0x1000)
+    lab, lp = _i32([1, 2])
+    # partials of 2000 items at a 151936-token vocabulary exceed the 16 MiB scratch
+    rc = lib.mis_score_labels_noalloc(ctypes.byref(seg), ctypes.c_void_p(0x1000), 64, ctypes.c_void_p(0x1000),
+                                      151936, mis.MIS_BF16, lp, 2, 0, ctypes.c_void_p(0x1000), None)
+    assert rc == mis.MIS_ERR_WORKSPACE and "scratch" in mis.last_error()
+    rc = lib.mis_score_labels_noalloc(ctypes.byref(seg), ctypes.c_void_p(0x1000), 64, ctypes.c_void_p(0x1000),
+                                      1000, mis.MIS_BF16, _i32([1000])[1], 1, 0, ctypes.c_void_p(0x1000), None)
+    assert rc == mis.MIS_ERR_LABEL
+    rc = lib.mis_score_labels_noalloc(ctypes.byref(seg), ctypes.c_void_p(0x1000), 64, ctypes.c_void_p(0x1000),
+                                      1000, mis.MIS_BF16, lp, 2, 0, None, None)
+    assert rc == mis.MIS_ERR_ARG

@@ -54,3 +54,17 @@ def test_single_request_scoring_figures():
     flops, nbytes = bench.lm_head_cost(wl)
     assert flops == 2 * 64 * 1024 * 151936 == 19_914_555_392
     assert nbytes == 2 * (151936 * 1024 + 64 * 1024) + 4 * 64 * 2 == 311_296_512
+
+
+def test_long_prefix_workload_figures():
+    # 4 requests: prefix 16384 + 256 items of 49 tokens, 64 query heads of 128
+    # dims; scoring H = 8192, V = 128256, K = 3 (the bench's default workload)
+    wl = workloads.config(5)
+    lq, s, n = 16384, 49, 256
+    pairs = 4 * (lq * (lq + 1) // 2 + n * (s * lq + s * (s + 1) // 2))
+    assert pairs == 1_360_241_664
+    assert bench.visible_pairs(wl) == pairs
+    assert bench.attention_flops(wl) == 4 * 128 * 64 * pairs == 44_572_398_845_952
+    flops, nbytes = bench.lm_head_cost(wl)
+    assert flops == 2 * 1024 * 8192 * 128256 == 2_151_778_615_296
+    assert nbytes == 2 * (128256 * 8192 + 1024 * 8192) + 4 * 1024 * 3

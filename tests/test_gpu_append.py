@@ -17,13 +17,11 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(autouse=True, params=["auto", "pipe", "pipe32", "classic"])
-def attention_kernel(request, monkeypatch):
+def attention_kernel(request):
     """Each bf16 attention kernel, forced, and the one chosen by shape."""
-    if request.param != "auto":
-        monkeypatch.setenv("MIS_ATTENTION_KERNEL", request.param)
-    else:
-        monkeypatch.delenv("MIS_ATTENTION_KERNEL", raising=False)
-    return request.param
+    mis.set_kernel_choice(attention=request.param)
+    yield request.param
+    mis.set_kernel_choice()
 
 
 def _item_mask(wl):

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import item_scoring_attention_amd as mis
 import oracle
 import workloads
 from gpu_common import (TOL_BF16_ATTN, TOL_F32, attention, build, cached, host, say, segments_oracle,
@@ -20,16 +21,14 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(autouse=True, params=["auto", "pipe", "pipe32", "classic"])
-def attention_kernel(request, monkeypatch):
+def attention_kernel(request):
     """Run every case with the bf16 kernel chosen by shape, and forced to each
     of the three kernels (the pipelined loop with 64 or with 32 query rows per
     wave, or the plain loop with two waves per SIMD); the fp32 cases do not
     depend on it."""
-    if request.param != "auto":
-        monkeypatch.setenv("MIS_ATTENTION_KERNEL", request.param)
-    else:
-        monkeypatch.delenv("MIS_ATTENTION_KERNEL", raising=False)
-    return request.param
+    mis.set_kernel_choice(attention=request.param)
+    yield request.param
+    mis.set_kernel_choice()
 
 
 def _err(got, ref):

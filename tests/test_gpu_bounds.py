@@ -6,7 +6,7 @@ nothing. The inputs here sit in allocations with 64 extra rows of bf16 NaN
 after the last token, and the kernels get views of the first T rows, so any
 read past the end puts a NaN into the output (a zero probability times a NaN
 value is NaN). Every access stays inside the allocation. The last request's
-length is 1 or 37 modulo 64, so its last key tile is mostly past the end.
+length is 1 or 9 modulo 64, so its last key tile is mostly past the end.
 """
 import numpy as np
 import pytest
@@ -23,13 +23,11 @@ PAD = 64
 
 
 @pytest.fixture(autouse=True, params=["auto", "pipe", "pipe32", "classic"])
-def attention_kernel(request, monkeypatch):
+def attention_kernel(request):
     """Each bf16 attention kernel, forced, and the one chosen by shape."""
-    if request.param != "auto":
-        monkeypatch.setenv("MIS_ATTENTION_KERNEL", request.param)
-    else:
-        monkeypatch.delenv("MIS_ATTENTION_KERNEL", raising=False)
-    return request.param
+    mis.set_kernel_choice(attention=request.param)
+    yield request.param
+    mis.set_kernel_choice()
 
 
 def _nan_padded(x: np.ndarray) -> torch.Tensor:

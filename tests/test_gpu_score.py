@@ -17,15 +17,13 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(autouse=True, params=["auto", "narrow", "wide4", "wide6"])
-def score_kernel(request, monkeypatch):
+def score_kernel(request):
     """Every case with the bf16 LM-head kernel chosen by shape (narrow tiles up
     to 64 items, else wide tiles with 3, 5 or 8 item blocks), and forced to the
     narrow tiles and to wide tiles of 4 and 6 item blocks."""
-    if request.param != "auto":
-        monkeypatch.setenv("MIS_SCORE_KERNEL", request.param)
-    else:
-        monkeypatch.delenv("MIS_SCORE_KERNEL", raising=False)
-    return request.param
+    mis.set_kernel_choice(score=request.param)
+    yield request.param
+    mis.set_kernel_choice()
 
 
 def _score(wl, seg, hid, W, labels, apply_softmax=False):
