@@ -69,6 +69,7 @@ struct LoopArgs {
   int rjt[2];       // last visible key of the lane's two query rows, minus 4g
   int rjb[2];       // first key of the rows' own item (0 for prefix rows), minus 4g
   int rlq;          // prefix length minus 4g
+  uint32_t sel;     // A operand of the row-sum MFMAs: bf16 (1, 1) or (0, 0), by lane
   int nvis, a_end, b_start, a_full;
   uint32_t kb_lo, kb_hi, vb_lo, vb_hi;  // this KV head's K and V at the request start
   uint32_t rb64, nrec;                  // 64 token rows in bytes; descriptor range
@@ -91,6 +92,7 @@ struct LoopArgs {
     [ka2] "v"(x.ka[2]), [ka3] "v"(x.ka[3]), [ka4] "v"(x.ka[4]), [ka5] "v"(x.ka[5]), [ka6] "v"(x.ka[6]),            \
     [ka7] "v"(x.ka[7]), [va0] "v"(x.va[0]), [va1] "v"(x.va[1]), [va2] "v"(x.va[2]), [va3] "v"(x.va[3]), KV,        \
     [rjt0] "v"(x.rjt[0]), [rjt1] "v"(x.rjt[1]), [rjb0] "v"(x.rjb[0]), [rjb1] "v"(x.rjb[1]), [rlq] "v"(x.rlq),     \
+    [sel] "v"(x.sel),                                                                                             \
     [nvis] "s"(x.nvis), [a_end] "s"(x.a_end), [b_start] "s"(x.b_start), [a_full] "s"(x.a_full),                   \
     [kb_lo] "s"(x.kb_lo), [kb_hi] "s"(x.kb_hi), [vb_lo] "s"(x.vb_lo), [vb_hi] "s"(x.vb_hi), [rb64] "s"(x.rb64),    \
     [nrec] "s"(x.nrec), [wlds] "s"(x.wlds), [c] "s"(x.c)                                                          \
@@ -101,7 +103,8 @@ struct LoopArgs {
   : [q0] "{a[64:95]}"(q0), [ka0] "v"(x.ka[0]), [ka1] "v"(x.ka[1]), [ka2] "v"(x.ka[2]), [ka3] "v"(x.ka[3]),         \
     [ka4] "v"(x.ka[4]), [ka5] "v"(x.ka[5]), [ka6] "v"(x.ka[6]), [ka7] "v"(x.ka[7]), [va0] "v"(x.va[0]),            \
     [va1] "v"(x.va[1]), [va2] "v"(x.va[2]), [va3] "v"(x.va[3]), MIS_ATTN_KV4, [rjt0] "v"(x.rjt[0]),               \
-    [rjb0] "v"(x.rjb[0]), [rlq] "v"(x.rlq), [nvis] "s"(x.nvis), [a_end] "s"(x.a_end), [b_start] "s"(x.b_start),   \
+    [rjb0] "v"(x.rjb[0]), [rlq] "v"(x.rlq), [sel] "v"(x.sel), [nvis] "s"(x.nvis), [a_end] "s"(x.a_end),          \
+    [b_start] "s"(x.b_start),                                                                                     \
     [a_full] "s"(x.a_full), [kb_lo] "s"(x.kb_lo), [kb_hi] "s"(x.kb_hi), [vb_lo] "s"(x.vb_lo),                     \
     [vb_hi] "s"(x.vb_hi), [rb64] "s"(x.rb64), [nrec] "s"(x.nrec), [wlds] "s"(x.wlds), [c] "s"(x.c)                \
   : MIS_ATTN_LOOP_CLOBBERS_QB1
@@ -260,6 +263,12 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
   x.wlds = lds0 + wrow * 256u;
   x.c = c;
   x.rlq = lq - 4 * g;
+  // Row sums on v_mfma_f32_16x16x32_bf16 with P^T as the B operand: lane
+  // l's A values select the k-groups (lanes / 16) of the same parity as its
+  // output rows' group, so each lane's accumulator holds its own query's
+  // sum: A[m][k] = 1 where (k / 8) % 2 == (m / 4) % 2, and lane l holds
+  // A[l % 16][8 (l / 16) ..].
+  x.sel = (((lane >> 4) ^ (lane >> 2)) & 1) == 0 ? 0x3f803f80u : 0u;
 
   // Every wave's zero stores are in LDS before any load lands there (an LDS
   // wait and a barrier; no fence, which would wait for vector memory too).

@@ -35,12 +35,20 @@ set_layout gives both variants' maps):
   v[64:79]   P_A   (P^T bf16, [qb][ks] 4 dwords each)
   v[80:95]   P_B
   then the K and V^T fragment rings (RING x 4 each), exp temporaries,
-  mask / rescale temporaries, m, the overflow-check maxima and bf16 ones
+  mask / rescale temporaries, m, the overflow-check maxima and the
+  row-sum selection operand
   a[0:127]   O^T accumulators [qb][db] (operands, pinned)
   a[128:191] Q^T fragments [qb][dstep] (operands, pinned)
-  a[192:223] row sums: 1^T P^T on the matrix cores, so they add exactly the
-             bf16 P that O^T += V^T P^T uses (every row of the 32 x 32
-             accumulator holds the sums; the block returns element 0)
+  a[192:199] row sums [qb], 4 each: on the matrix cores, so they add exactly
+             the bf16 P that O^T += V^T P^T uses. One v_mfma_f32_16x16x32_bf16
+             per 16-key quad of P^T: read as its B operand, lane l's 8 values
+             are column l % 16, k-group l / 16 (lanes ql and ql + 32 of query
+             ql land in k-groups of equal parity, parity ql / 16). The A
+             operand selects k-groups of parity (m / 4) % 2 for output row m,
+             and lane l holds rows 4 (l / 16) .. +3: so all four accumulator
+             registers of lane l hold the sum of the lane's own query ql
+             (half the matrix-pipe time of 1^T P^T on a 32 x 32 MFMA, with
+             the same per-lane rescale)
 """
 from __future__ import annotations
 
@@ -75,7 +83,7 @@ def set_layout(qb: int):
     """Register map for QB query blocks of 32 rows per wave (2: 64 rows, the
     map in the module docstring; 1: 32 rows, small enough for two waves per
     SIMD: S 0-31, P 32-47, 3-deep rings from 48, 8 exp temporaries that the
-    rescale path reuses; O^T a[0:63], Q^T a[64:95], row sums a[96:111])."""
+    rescale path reuses; O^T a[0:63], Q^T a[64:95], row sums a[96:99])."""
     global QB, RING, S_A, S_B, P_A, P_B, KB, VB, E0, NPT, X0, VM, VMX, VNINF, ONES, NUM_V, QA, LS
     QB = qb
     RING = 4 if qb == 2 else 3         # K and V^T fragments in flight (each ring slot is 4 VGPRs)
@@ -93,10 +101,10 @@ def set_layout(qb: int):
     VM = (rest, rest + 1)              # running maxima m (exp2 domain)
     VMX = (rest + 2, rest + 3)         # largest P of the current sub-tile (overflow check)
     VNINF = rest + 4                   # -inf
-    ONES = rest + 8                    # 4 VGPRs of bf16 ones: the A operand of the row-sum MFMAs
+    ONES = rest + 8                    # 4 VGPRs of bf16 0/1 (lane pattern): A operand of the row-sum MFMAs
     NUM_V = rest + 12
     QA = 64 * qb                       # Q^T fragments a[QA:QA + 32 qb]
-    LS = 96 * qb                       # row-sum accumulators [qb], 16 AGPRs each
+    LS = 96 * qb                       # row-sum accumulators [qb], 4 AGPRs each
 
 
 set_layout(2)
@@ -118,6 +126,7 @@ S_VRSRC = 64  # V buffer descriptor s[64:67]
 SGPRS = list(range(40, 72))
 
 MFMA = "v_mfma_f32_32x32x16_bf16"
+MFMA_RS = "v_mfma_f32_16x16x32_bf16"  # row sums (half the cycles of MFMA)
 # VALU cycles placed after each MFMA (one v_mfma_f32_32x32x16_bf16 keeps the
 # matrix pipe busy for 32 cycles; an exp costs about 10 issue cycles, other
 # VALU 4) and before the first one (while the first K fragment arrives).
@@ -172,7 +181,7 @@ def softmax_graph(s_cur: int, p_cur: int, c: str):
     two FMAs (c s - m), two exps, a convert into dword pi of P_cur[qb] and a
     max3 into VMX[qb]. Pair i uses exp temporaries E0 + 2 (i % NPT), so
     pair i + NPT waits for pair i's convert and max (write after read). The row
-    sums are not formed here: 1^T P^T runs on the matrix cores."""
+    sums are not formed here: they run on the matrix cores."""
     nodes = []
 
     def add(text, cost, deps):
@@ -290,8 +299,8 @@ def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c, side=()):
                 v_read(f + RING)
             if qb == QB - 1 and db == 3:
                 for q in range(QB):
-                    ls = ar(LS + 16 * q, 16)
-                    b.emit(f"{MFMA} {ls}, {vr(ONES, 4)}, {vr(p_prev + 8 * q + 4 * ks, 4)}, {ls}")
+                    ls = ar(LS + 4 * q, 4)
+                    b.emit(f"{MFMA_RS} {ls}, {vr(ONES, 4)}, {vr(p_prev + 8 * q + 4 * ks, 4)}, {ls}")
         if slot >= 1 and side:
             for ln in side.pop(0):
                 b.emit(ln)
@@ -355,7 +364,7 @@ def slow_path(b: Block, s_cur, p_cur, c, label, ret, first=False):
             b.emit(f"s_cmp_eq_u32 {sr(S_T)}, 0")
             b.emit(f"s_cbranch_scc1 {label}_nr{qb}")
         tmps = [X0 + 4, X0 + 5, X0 + 6, X0 + 7]
-        for i, acc in enumerate(list(range(64 * qb, 64 * qb + 64)) + list(range(LS + 16 * qb, LS + 16 * qb + 16))):
+        for i, acc in enumerate(list(range(64 * qb, 64 * qb + 64)) + list(range(LS + 4 * qb, LS + 4 * qb + 4))):
             t = tmps[i % 4]
             b.emit(f"v_accvgpr_read_b32 {vr(t)}, {ar(acc)}")
             b.emit(f"v_mul_f32 {vr(t)}, {vr(t)}, {vr(al)}")
@@ -445,8 +454,8 @@ def pv_tail(b: Block, p_prev: int, voff: int):
             b.emit(f"{MFMA} {o}, {vr(VB[g % RING], 4)}, {vr(p_prev + 8 * qb + 4 * gks, 4)}, {o}")
     for ks in range(2):
         for q in range(QB):
-            ls = ar(LS + 16 * q, 16)
-            b.emit(f"{MFMA} {ls}, {vr(ONES, 4)}, {vr(p_prev + 8 * q + 4 * ks, 4)}, {ls}")
+            ls = ar(LS + 4 * q, 4)
+            b.emit(f"{MFMA_RS} {ls}, {vr(ONES, 4)}, {vr(p_prev + 8 * q + 4 * ks, 4)}, {ls}")
 
 
 def loop_block(dpw: int, stages: int) -> list[str]:
@@ -458,12 +467,12 @@ def loop_block(dpw: int, stages: int) -> list[str]:
         b.emit(f"v_accvgpr_write_b32 {ar(i)}, 0")
     for i in range(8 * QB):
         b.emit(f"v_mov_b32 {vr(P_B + i)}, 0")
-    for i in range(16 * QB):
+    for i in range(4 * QB):
         b.emit(f"v_accvgpr_write_b32 {ar(LS + i)}, 0")
     for qb in range(QB):
         b.emit(f"v_mov_b32 {vr(VM[qb])}, 0xf149f2ca")  # -1e30
     for i in range(4):
-        b.emit(f"v_mov_b32 {vr(ONES + i)}, 0x3f803f80")  # bf16 (1, 1)
+        b.emit(f"v_mov_b32 {vr(ONES + i)}, %[sel]")  # bf16 (1, 1) or (0, 0) by lane
     b.emit(f"v_mov_b32 {vr(VNINF)}, 0xff800000")
     b.emit(f"s_mov_b32 {sr(S_LIM)}, 0x4b800000")  # 2^24
     b.emit(f"s_mov_b32 {sr(S_T)}, 0")
@@ -540,7 +549,7 @@ def loop_block(dpw: int, stages: int) -> list[str]:
         b.emit("s_nop 7")
     b.emit(f"v_accvgpr_read_b32 %[l0], {ar(LS)}")
     if QB == 2:
-        b.emit(f"v_accvgpr_read_b32 %[l1], {ar(LS + 16)}")
+        b.emit(f"v_accvgpr_read_b32 %[l1], {ar(LS + 4)}")
     b.emit("s_branch L_end")
     for i, args in enumerate(slow):
         slow_path(b, *args[:2], c, *args[2:], first=(i == 0))
@@ -580,7 +589,7 @@ def prologue_block(dpw: int, stages: int) -> list[str]:
 def clobbers() -> list[str]:
     regs = [f'"v{i}"' for i in range(NUM_V)]
     regs += [f'"s{i}"' for i in SGPRS]
-    regs += [f'"a{i}"' for i in range(LS, LS + 16 * QB)]
+    regs += [f'"a{i}"' for i in range(LS, LS + 4 * QB)]
     regs += ['"vcc"', '"scc"', '"m0"', '"memory"']
     return regs
 
