@@ -147,11 +147,11 @@ __device__ __forceinline__ void attn_loop_qb1(const LoopArgs &x, const f32x32 &q
 
 // HP heads x TB row blocks per workgroup, one wave each: TB = 1 gives a wave
 // 64 query rows (two 32-row query blocks, one wave per SIMD), TB = 2 gives it
-// 32 rows (two waves per SIMD). K/V stages of the ring: three when one
-// workgroup holds the CU (HP = 4, TB = 1: 96 KB of LDS), two when two
+// 32 rows (two waves per SIMD). K/V stages of the ring: four when one
+// workgroup holds the CU (HP = 4, TB = 1: 128 KB of LDS), two when two
 // workgroups share it (64 KB each).
 template <int HP, int TB>
-constexpr int kStages = HP == 4 && TB == 1 ? 3 : 2;
+constexpr int kStages = HP == 4 && TB == 1 ? 4 : 2;
 
 template <int HP, int TB>
 __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(

@@ -243,26 +243,47 @@ def schedule(nodes, slots: int, budget: int, head_budget: int):
     return out
 
 
-def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c, side=()):
+def k_read(b: Block, ds: int, koff: int, tag: str):
+    b.ds_op(tag, f"ds_read_b128 {vr(KB[ds % RING], 4)}, %[ka{ds}] offset:{koff}")
+
+
+def v_read(b: Block, f: int, voff: int, tag: str):
+    ks, db = divmod(f, 4)
+    buf = VB[f % RING]
+    off = voff + 4096 * ks
+    b.ds_op(tag, f"ds_read_b64_tr_b16 {vr(buf, 2)}, %[va{db}] offset:{off}")
+    b.ds_op(tag, f"ds_read_b64_tr_b16 {vr(buf + 2, 2)}, %[va{db}] offset:{off + 2048}")
+
+
+def hoist_first_reads(b: Block, koff: int, voff: int):
+    """The first RING K and V fragment reads of a step, issued ahead of it
+    (tagged N..., picked up by the step as its own)."""
+    for ds in range(RING):
+        k_read(b, ds, koff, f"Nk{ds}")
+    for f in range(RING):
+        v_read(b, f, voff, f"Nv{f}")
+
+
+def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c, side=(), pre=False, nxt=None):
     """One pipelined sub-tile: QK(next) + PV(prev) MFMAs interleaved with softmax(cur).
 
-    `side` holds small instruction groups (the next tiles' LDS-direct loads)
-    issued one after each MFMA from the second on, so their issue cost hides
-    under the matrix pipe."""
-    b.reset_ds()
+    `side` holds small instruction groups (descriptor set-up and the next
+    tiles' LDS-direct loads) issued one after each MFMA from the second on,
+    so their issue cost hides under the matrix pipe. `pre`: the step's first
+    RING K and V fragment reads were issued ahead of it (by the previous step
+    or the block's start). `nxt` = (koff, voff) of the next step: its first
+    RING fragments are read here as soon as their ring slots are free, so
+    the next step's first MFMA does not wait for a read issued at its start."""
+    if pre:
+        # the fragments read ahead are all this step tracks; everything
+        # issued before them has completed (LDS reads complete in order)
+        b.ds = [t[1:] for t in b.ds if t.startswith("N")]
+        b.done = 0
+    else:
+        b.reset_ds()
     side = list(side)
     valu = schedule(softmax_graph(s_cur, p_cur, c), 16 * QB, SLOT_BUDGET, HEAD_BUDGET)
     vi = 0
-
-    def k_read(ds):
-        b.ds_op(f"k{ds}", f"ds_read_b128 {vr(KB[ds % RING], 4)}, %[ka{ds}] offset:{koff}")
-
-    def v_read(f):
-        ks, db = divmod(f, 4)
-        buf = VB[f % RING]
-        off = voff + 4096 * ks
-        b.ds_op(f"v{f}", f"ds_read_b64_tr_b16 {vr(buf, 2)}, %[va{db}] offset:{off}")
-        b.ds_op(f"v{f}", f"ds_read_b64_tr_b16 {vr(buf + 2, 2)}, %[va{db}] offset:{off + 2048}")
 
     def valu_group():
         nonlocal vi
@@ -271,10 +292,11 @@ def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c, side=()):
                 b.emit(ln)
             vi += 1
 
-    for ds in range(RING):
-        k_read(ds)
-    for f in range(RING):
-        v_read(f)
+    if not pre:
+        for ds in range(RING):
+            k_read(b, ds, koff, f"k{ds}")
+        for f in range(RING):
+            v_read(b, f, voff, f"v{f}")
     valu_group()
     # MFMA order: all QK then all PV, or (ILV) alternating, so that the QK
     # accumulation chain of a single query block never runs back to back
@@ -288,7 +310,9 @@ def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c, side=()):
             src_c = "0" if ds == 0 else acc
             b.emit(f"{MFMA} {acc}, {vr(KB[ds % RING], 4)}, {ar(QA + 32 * qb + 4 * ds, 4)}, {src_c}")
             if qb == QB - 1 and ds + RING < 8:
-                k_read(ds + RING)
+                k_read(b, ds + RING, koff, f"k{ds + RING}")
+            elif qb == QB - 1 and nxt:  # last use of this ring slot: the next step's fragment
+                k_read(b, ds % RING, nxt[0], f"Nk{ds % RING}")
         else:
             f, qb = divmod(idx, QB)
             ks, db = divmod(f, 4)
@@ -296,7 +320,9 @@ def step(b: Block, s_cur, s_next, p_cur, p_prev, koff, voff, c, side=()):
             o = ar(16 * (4 * qb + db), 16)
             b.emit(f"{MFMA} {o}, {vr(VB[f % RING], 4)}, {vr(p_prev + 8 * qb + 4 * ks, 4)}, {o}")
             if qb == QB - 1 and f + RING < 8:
-                v_read(f + RING)
+                v_read(b, f + RING, voff, f"v{f + RING}")
+            elif qb == QB - 1 and nxt:
+                v_read(b, f % RING, nxt[1], f"Nv{f % RING}")
             if qb == QB - 1 and db == 3:
                 for q in range(QB):
                     ls = ar(LS + 4 * q, 4)
@@ -388,16 +414,27 @@ def dma_setup(b: Block, vis_add: int, is_k: bool, rsrc: int):
     """Buffer descriptor of visit S_T + vis_add: K or V rows of its key tile up
     to the request end; a zero range when the visit does not exist (the loads
     then touch no memory and write nothing)."""
+    for ln in dma_setup_lines(vis_add, is_k, rsrc):
+        b.emit(ln)
+
+
+def dma_setup_lines(vis_add: int, is_k: bool, rsrc: int) -> list[str]:
     base_lo, base_hi = ("%[kb_lo]", "%[kb_hi]") if is_k else ("%[vb_lo]", "%[vb_hi]")
-    b.emit(f"s_add_u32 {sr(S_NV1)}, {sr(S_T)}, {vis_add}")
-    tile_of(b, S_LAST, sr(S_NV1))
-    b.emit(f"s_mul_i32 {sr(S_OFF)}, {sr(S_LAST)}, %[rb64]")
-    b.emit(f"s_add_u32 {sr(rsrc)}, {base_lo}, {sr(S_OFF)}")
-    b.emit(f"s_addc_u32 {sr(rsrc + 1)}, {base_hi}, 0")
-    b.emit(f"s_sub_u32 {sr(rsrc + 2)}, %[nrec], {sr(S_OFF)}")
-    b.emit(f"s_cmp_lt_u32 {sr(S_NV1)}, %[nvis]")
-    b.emit(f"s_cselect_b32 {sr(rsrc + 2)}, {sr(rsrc + 2)}, 0")
-    b.emit(f"s_mov_b32 {sr(rsrc + 3)}, 0x20000")
+    t = Block()
+    t.emit(f"s_add_u32 {sr(S_NV1)}, {sr(S_T)}, {vis_add}")
+    tile_of(t, S_LAST, sr(S_NV1))
+    t.emit(f"s_mul_i32 {sr(S_OFF)}, {sr(S_LAST)}, %[rb64]")
+    t.emit(f"s_add_u32 {sr(rsrc)}, {base_lo}, {sr(S_OFF)}")
+    t.emit(f"s_addc_u32 {sr(rsrc + 1)}, {base_hi}, 0")
+    t.emit(f"s_sub_u32 {sr(rsrc + 2)}, %[nrec], {sr(S_OFF)}")
+    t.emit(f"s_cmp_lt_u32 {sr(S_NV1)}, %[nvis]")
+    t.emit(f"s_cselect_b32 {sr(rsrc + 2)}, {sr(rsrc + 2)}, 0")
+    t.emit(f"s_mov_b32 {sr(rsrc + 3)}, 0x20000")
+    return t.lines
+
+
+# scalar instructions of descriptor set-up placed after one MFMA
+SETUP_CHUNK = 4
 
 
 def dma_groups(is_k: bool, rsrc: int, lds_byte: int, dpw: int) -> list[list[str]]:
@@ -419,15 +456,23 @@ def dma_groups(is_k: bool, rsrc: int, lds_byte: int, dpw: int) -> list[list[str]
 
 def barrier_dma(b: Block, tp: int, dpw: int, stages: int) -> list[list[str]]:
     """At tile t' = S_T + tp: wait for the loads tile t' still needs, barrier
-    (every wave is done with K(t') and V(t'-1)), then set up the loads of
-    K(t' + STAGES) into K stage tp and V(t' + STAGES - 1) into V stage tp - 1.
-    Every barrier issues the same 2 dpw loads, so the loads still allowed in
-    flight (those of the previous barrier, with three stages) are a constant."""
-    b.emit(f"s_waitcnt vmcnt({2 * dpw * (stages - 2)})")
+    (every wave is done with K(t') and V(t'-1)); the returned side groups set
+    up and issue the loads of K(t' + STAGES) into K stage tp and
+    V(t' + STAGES - 1) into V stage tp - 1 during the next step. Every
+    barrier issues the same 2 dpw loads, so the loads still allowed in flight
+    are a constant: those of the last STAGES - 2 barriers, or with four
+    stages or more of the last STAGES - 3 (the steps then read K(t' + 1) and
+    V(t') before barrier t', so they must be complete by barrier t' - 1:
+    issued at barrier t' - 3, two visits earlier, as with three stages)."""
+    in_flight = stages - 3 if stages >= 4 else stages - 2
+    b.emit(f"s_waitcnt vmcnt({2 * dpw * in_flight})")
     b.emit("s_barrier")
-    dma_setup(b, tp + stages, True, S_RSRC)
-    dma_setup(b, tp + stages - 1, False, S_VRSRC)
-    return (dma_groups(True, S_RSRC, k_off(tp), dpw) +
+
+    def chunks(lines):
+        return [lines[i:i + SETUP_CHUNK] for i in range(0, len(lines), SETUP_CHUNK)]
+
+    return (chunks(dma_setup_lines(tp + stages, True, S_RSRC)) + dma_groups(True, S_RSRC, k_off(tp), dpw) +
+            chunks(dma_setup_lines(tp + stages - 1, False, S_VRSRC)) +
             dma_groups(False, S_VRSRC, v_lds((tp - 1) % stages, stages), dpw))
 
 
@@ -496,6 +541,8 @@ def loop_block(dpw: int, stages: int) -> list[str]:
             b.emit(f"{MFMA} {acc}, {vr(KB[g % RING], 4)}, {ar(QA + 32 * qb + 4 * g, 4)}, {acc}")
     for _ in range(3):
         b.emit("s_nop 7")
+    # the first step's first fragments (its PV reads the zeroed last V stage)
+    hoist_first_reads(b, k_off(0) + HALF, v_off(stages - 1) + HALF)
     # ---- main loop over groups of STAGES tiles (S_T a multiple of STAGES at the top)
     b.emit("L_loop:")
     pos = 0
@@ -512,16 +559,24 @@ def loop_block(dpw: int, stages: int) -> list[str]:
             if h == 0:  # QK: second half of tile t'; PV: second half of tile t' - 1
                 koff = k_off(tp) + HALF
                 voff = v_off((tp - 1) % stages) + HALF
+                # next: QK first half of tile t' + 1, PV first half of tile t'.
+                # Read ahead only with four stages: K(t' + 1) and V(t') are then
+                # complete and visible from the last barrier on (with fewer
+                # stages only after the coming one)
+                nxt = (k_off((tp + 1) % stages), v_off(tp)) if stages >= 4 else None
+                pre = True
             else:  # QK: first half of tile t' + 1; PV: first half of tile t'
                 koff = k_off((tp + 1) % stages)
                 voff = v_off(tp)
+                # next: tile t' + 1's h = 0 step (no barrier in between)
+                nxt = (k_off((tp + 1) % stages) + HALF, v_off(tp) + HALF)
+                pre = stages >= 4
             b.emit(f"s_add_u32 {sr(S_NV1)}, {sr(S_T)}, {tp}")
             b.emit(f"s_cmp_ge_u32 {sr(S_NV1)}, %[a_full]")
             b.emit(f"s_cbranch_scc1 L_mask{pos}")
             b.emit(f"L_nomask{pos}:")
             masks.append((s_cur, h, pos))
-            b.emit("s_waitcnt lgkmcnt(0)")
-            step(b, s_cur, s_next, p_cur, p_prev, koff, voff, c, side)
+            step(b, s_cur, s_next, p_cur, p_prev, koff, voff, c, side, pre=pre, nxt=nxt)
             side = []
             b.emit(f"v_cmp_lt_f32 vcc, {sr(S_LIM)}, {vr(VMX[0])}")
             if QB == 2:
@@ -564,8 +619,11 @@ def loop_block(dpw: int, stages: int) -> list[str]:
 
 def prologue_order(stages: int) -> list[tuple[int, bool]]:
     """The loads the barriers of visits -STAGES+1 .. -1 would have issued, K(0)
-    first: K(0), K(1), V(0), then (three stages) K(2), V(1)."""
-    return [(0, True), (1, True), (0, False)] + ([(2, True), (1, False)] if stages == 3 else [])
+    first: K(0), then K(j), V(j - 1) for j = 1 .. STAGES - 1."""
+    out = [(0, True)]
+    for j in range(1, stages):
+        out += [(j, True), (j - 1, False)]
+    return out
 
 
 def prologue_block(dpw: int, stages: int) -> list[str]:
@@ -601,7 +659,7 @@ HEADER = """// Generated by gen_attn_loop.py; do not edit by hand.
 
 
 # (macro suffix, LDS-direct loads per wave and tile, K/V stages, query blocks per wave)
-VARIANTS = (("DPW4", 4, 3, 2), ("DPW8", 8, 2, 2), ("QB1", 4, 2, 1))
+VARIANTS = (("DPW4", 4, 4, 2), ("DPW8", 8, 2, 2), ("QB1", 4, 2, 1))
 
 
 def render() -> str:
