@@ -237,6 +237,10 @@ def schedule(nodes, slots: int, budget: int, head_budget: int):
         while g < slots and load[g] + cost > cap(g):
             g += 1
         g = min(g, slots)
+        # a consumer in its producer's group would lose the MFMA between them
+        # (exp latency and the transcendental-use hazard): refuse the budget
+        if any(group[d] >= g for d in deps):
+            raise ValueError(f"VALU budget {budget} leaves no MFMA between {text!r} and its producer")
         group[n] = g
         load[g] += cost
         out[g].append(text)
