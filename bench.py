@@ -183,16 +183,47 @@ def cpu_baseline(wl, q, k, v, hid, W, labels, budget_s: float, flops: float):
     }
 
 
-def sweep(args) -> int:
-    """Request-size sweep: one packed MIS request against single-item scoring.
+def layout(wl, requests):
+    """Row map and metadata of a packed batch built from a member batch's rows.
 
-    For each N, the items are scored (a) packed behind one shared prefix in a
-    single request (MIS) and (b) as N separate requests [q; c_i], each with
-    its own copy of the prefix, in one batched call (SIS). Both run the full
-    step (segments, attention, label scores) on the same model shape as the
-    single-request workload; the prefix is 744 tokens (the mean prompt length
-    From Generation to Scoring reports for its profile set) and each item 24 tokens plus its
-    delimiter (the compact prompt).
+    ``requests`` lists (member, item indices) pairs; each becomes one request
+    made of the member's query rows followed by those items' rows. Returns
+    (rows, cu_seqlens, prefix_lens, cu_items, item_starts) with ``rows`` the
+    source row of every packed token."""
+    lens = wl.item_lengths()
+    rows, cu, pl, ci, st = [], [0], [], [0], []
+    for r, items in requests:
+        base, lq = int(wl.cu_seqlens[r]), int(wl.prefix_lens[r])
+        rows.append(np.arange(base, base + lq))
+        off = lq
+        for i in items:
+            g = int(wl.cu_items[r]) + int(i)
+            s0 = base + int(wl.item_starts[g])
+            rows.append(np.arange(s0, s0 + int(lens[g])))
+            st.append(off)
+            off += int(lens[g])
+        cu.append(cu[-1] + off)
+        pl.append(lq)
+        ci.append(ci[-1] + len(items))
+    return (np.concatenate(rows), np.asarray(cu, np.int32), np.asarray(pl, np.int32), np.asarray(ci, np.int32),
+            np.asarray(st, np.int32))
+
+
+def paper(args) -> int:
+    """MIS against single-item scoring on the profile-labeling benchmark's shape.
+
+    From Generation to Scoring, §6.1: members' queries of mean 744 tokens
+    (median 543, p95 2,047), items of about 28 tokens (chat layout; 24 in the
+    compact layout of §3.1), 200 candidates per member; §6.4 sweeps the items
+    per request N from 1 to 200 and splits 200 candidates into two requests of
+    100. Here a batch of members (one seeded draw) is scored, whole step each
+    (segments, attention, label scores), as
+      mis:    one request per member holding its N items behind its query;
+      split:  two requests per member of N/2 items, the query in each (N = 200);
+      single: one request [q; c_i] per item (no prefix reuse across requests).
+    Every layout is gathered on the GPU from the same rows, so all score the
+    same values. Reported beside each measured speedup: the prefill-token
+    ratio of the batch and Eq. 5's R(N) with the workload ratio 744 / 28.
     """
     import torch
 
@@ -200,71 +231,83 @@ def sweep(args) -> int:
     import workloads
 
     torch.cuda.set_device(0)
-    base = workloads.config(2)
-    lq, item_len = 744, 25
+    nmax = 200
+    wl = workloads.paper_batch(args.members, nmax, args.item_tokens)
+    print(f"[paper] {wl.description}: T={wl.total_tokens}", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
 
     def dev(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
 
-    def run(wl, steps):
-        q, k, v = workloads.qkv(wl)
-        qd, kd, vd = dev(q), dev(k), dev(v)
-        bm, bn = mis.mis_attention_tile_shape(mis.MIS_BF16, wl.hq, wl.hkv, wl.d)
-        seg_buf = torch.empty(mis.mis_segments_bytes(wl.cu_seqlens, wl.total_items, bm, bn),
-                              dtype=torch.uint8, device="cuda")
-        seg = mis.mis_build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, bm, bn,
-                                     dev_buf=seg_buf)
-        hid = np.zeros((wl.total_tokens, wl.hidden), dtype=np.uint16)
-        hid[seg.array("readout_pos").cpu().numpy()] = workloads.readout_values(wl)
-        hidd, Wd = dev(hid), dev(workloads.lm_head(wl))
-        labels = workloads.label_ids(wl)
-        scores = torch.empty((wl.total_items, wl.num_labels), dtype=torch.float32, device="cuda")
-        ws = torch.empty(mis.mis_score_workspace_bytes(wl.total_items, wl.vocab, wl.num_labels, wl.hidden,
-                                                       mis.MIS_BF16), dtype=torch.uint8, device="cuda")
-        o = torch.empty_like(qd)
+    q, k, v = workloads.qkv(wl)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    seg = mis.mis_build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, 64, 64)
+    hid = np.zeros((wl.total_tokens, wl.hidden), dtype=np.uint16)
+    hid[seg.array("readout_pos").cpu().numpy()] = workloads.readout_values(wl)
+    hidd, Wd = dev(hid), dev(workloads.lm_head(wl))
+    labels = workloads.label_ids(wl)
+    del q, k, v, hid
+    bm, bn = mis.mis_attention_tile_shape(mis.MIS_BF16, wl.hq, wl.hkv, wl.d)
+    rho = workloads.PAPER_QUERY_MEAN / args.item_tokens
+
+    def run(requests):
+        rows, cu, pl, ci, st = layout(wl, requests)
+        idx = torch.from_numpy(rows).cuda()
+        qx, kx, vx, hx = qd[idx], kd[idx], vd[idx], hidd[idx]
+        ox = torch.empty_like(qx)
+        T, N = int(cu[-1]), int(ci[-1])
+        seg_buf = torch.empty(mis.mis_segments_bytes(cu, N, bm, bn), dtype=torch.uint8, device="cuda")
+        scores = torch.empty((N, wl.num_labels), dtype=torch.float32, device="cuda")
+        ws = torch.empty(mis.mis_score_workspace_bytes(N, wl.vocab, wl.num_labels, wl.hidden, mis.MIS_BF16),
+                         dtype=torch.uint8, device="cuda")
 
         def step():
-            sg = mis.mis_build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, bm, bn,
-                                        dev_buf=seg_buf, stream=stream)
-            mis.mis_attention_prefill(sg, qd, kd, vd, o=o, stream=stream)
-            mis.mis_score_labels(sg, hidd, Wd, labels, scores=scores, ws=ws, stream=stream)
+            s = mis.mis_build_segments(cu, pl, ci, st, bm, bn, dev_buf=seg_buf, stream=stream)
+            mis.mis_attention_prefill(s, qx, kx, vx, o=ox, stream=stream)
+            mis.mis_score_labels(s, hx, Wd, labels, scores=scores, ws=ws, stream=stream)
 
-        for _ in range(3):
+        for _ in range(2):
             step()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
+        for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        lens = np.diff(cu)
+        pairs = int(sum(int(a) * (int(a) + 1) // 2 for a in pl))
+        for r in range(len(pl)):
+            s_items = np.diff(np.append(st[ci[r]:ci[r + 1]], lens[r])).astype(np.int64)
+            pairs += int((s_items * int(pl[r]) + s_items * (s_items + 1) // 2).sum())
+        return {"requests": len(pl), "tokens": T, "items": N, "ms_per_step": round(ms, 4),
+                "item_scores_per_s": round(N / (ms * 1e-3), 1),
+                "prefill_tokens_per_label": round(T / N, 2),
+                "attention_tflop": round(4 * wl.d * wl.hq * pairs / 1e12, 4)}
 
+    members = range(wl.num_requests)
     rows = []
-    for n in (1, 5, 20, 50, 100, 200):
-        kw = dict(hq=base.hq, hkv=base.hkv, d=base.d, hidden=base.hidden, vocab=base.vocab,
-                  num_labels=base.num_labels, seed=7)
-        wl_mis = workloads.from_lengths(f"sweep-mis-{n}", [lq], [[item_len] * n], **kw)
-        wl_sis = workloads.from_lengths(f"sweep-sis-{n}", [lq] * n, [[item_len]] * n, **kw)
-        t_mis, t_sis = run(wl_mis, args.steps), run(wl_sis, args.steps)
-        rows.append({
-            "items": n,
-            "mis_ms_per_step": round(t_mis * 1e3, 4),
-            "sis_ms_per_step": round(t_sis * 1e3, 4),
-            "mis_item_scores_per_s": round(n / t_mis, 1),
-            "sis_item_scores_per_s": round(n / t_sis, 1),
-            "speedup": round(t_sis / t_mis, 3),
-            "mis_prefill_tokens_per_item": round((lq + n * item_len) / n, 1),
-            "sis_prefill_tokens_per_item": lq + item_len,
-            "mis_attention_gflop": round(attention_flops(wl_mis) / 1e9, 3),
-            "sis_attention_gflop": round(attention_flops(wl_sis) / 1e9, 3),
-        })
-        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    for n in args.paper_n:
+        line = {"items_per_member": n}
+        line["mis"] = run([(r, range(n)) for r in members])
+        line["single"] = run([(r, [i]) for r in members for i in range(n)])
+        if n == nmax:
+            line["split_2x100"] = run([(r, range(h * n // 2, (h + 1) * n // 2)) for r in members for h in (0, 1)])
+            line["split_vs_mis"] = round(line["mis"]["ms_per_step"] / line["split_2x100"]["ms_per_step"], 3)
+        line["speedup_vs_single"] = round(line["single"]["ms_per_step"] / line["mis"]["ms_per_step"], 3)
+        line["prefill_token_ratio"] = round(line["single"]["tokens"] / line["mis"]["tokens"], 3)
+        line["R_eq5_workload"] = round(n * (1 + rho) / (n + rho), 3)
+        rows.append(line)
+        print(json.dumps(line), file=sys.stderr, flush=True)
     print(json.dumps({
-        "metric": "MIS vs single-item scoring, whole step, 1 GPU", "unit": "item scores/s",
-        "steps": args.steps, "data": "synthetic",
-        "config": {"workload": "request-size sweep", "prefix": lq, "item_tokens": item_len,
-                   "hq": base.hq, "hkv": base.hkv, "head_dim": base.d, "hidden": base.hidden,
-                   "vocab": base.vocab, "labels": base.num_labels},
+        "metric": "MIS vs single-item scoring on the profile-labeling shape, whole step, 1 GPU",
+        "unit": "item scores/s", "steps": args.steps, "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "members": wl.num_requests,
+                   "item_tokens": args.item_tokens, "seed": wl.seed,
+                   "query_lengths": {"mean": float(np.mean(wl.prefix_lens)),
+                                     "median": float(np.median(wl.prefix_lens)),
+                                     "p95": float(np.percentile(wl.prefix_lens, 95))},
+                   "hq": wl.hq, "hkv": wl.hkv, "head_dim": wl.d, "hidden": wl.hidden, "vocab": wl.vocab,
+                   "labels": wl.num_labels},
         "sweep": rows}), flush=True)
     return 0
 
@@ -317,8 +360,13 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle attention work")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="steps timed after a 512 MB write between steps (cold caches); 0 skips them")
-    ap.add_argument("--sweep", action="store_true",
-                    help="request-size sweep (N = 1 .. 200 items): packed MIS against single-item scoring")
+    ap.add_argument("--paper", "--sweep", action="store_true", dest="paper",
+                    help="the profile-labeling benchmark's shape: MIS against single-item scoring and the 2 x 100 "
+                         "split for N = 1 .. 200 items per member")
+    ap.add_argument("--members", type=int, default=32, help="members in the --paper batch")
+    ap.add_argument("--item-tokens", type=int, default=28, help="item length in --paper (28 chat, 24 compact)")
+    ap.add_argument("--paper-n", type=lambda x: [int(t) for t in x.split(",")], default=[1, 5, 20, 50, 100, 200],
+                    help="items per member in --paper")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args(argv)
@@ -336,8 +384,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    if args.sweep:
-        return sweep(args)
+    if args.paper:
+        return paper(args)
     torch.cuda.set_device(0)
     wl = workloads.config(args.config)
     if wl.dtype != "bf16" or not wl.has_scoring:

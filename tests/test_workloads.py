@@ -1,5 +1,6 @@
 """Seeded input generators: determinism, bf16 rounding, and the five workload shapes."""
 import numpy as np
+import pytest
 import torch
 
 import workloads
@@ -66,3 +67,42 @@ def test_labels_distinct_and_in_range():
         lab = workloads.label_ids(wl)
         assert len(set(lab.tolist())) == wl.num_labels
         assert lab.min() >= 0 and lab.max() < wl.vocab
+
+
+def test_paper_query_lengths_match_the_quoted_statistics():
+    # From Generation to Scoring, §6.1: median 543, mean 744, 95th percentile 2,047
+    x = workloads.paper_query_lengths(400_000, 6)
+    assert abs(np.median(x) - 543) <= 3
+    assert abs(x.mean() - 744) / 744 < 0.01
+    assert 1950 <= np.percentile(x, 95) <= 2050
+    assert x.min() >= 1
+
+
+def test_paper_query_lengths_stratified():
+    x = workloads.paper_query_lengths(32, 6, stratified=True)
+    assert np.median(x) == 543 and abs(x.mean() - 744) / 744 < 0.03
+    assert sorted(x) == sorted(workloads.paper_query_lengths(32, 7, stratified=True))  # same quantiles
+    assert not np.array_equal(x, workloads.paper_query_lengths(32, 7, stratified=True))  # another order
+
+
+def test_paper_batch_request_sizes():
+    # about 6,400 tokens per member at N = 200 items of 28 tokens (§6.1)
+    wl = workloads.paper_batch(64, 200, 28)
+    assert wl.total_items == 64 * 200
+    assert np.all(wl.item_lengths() == 28)
+    assert abs(wl.total_tokens / 64 - 6344) / 6344 < 0.15
+
+
+def test_bench_layouts_regroup_the_same_rows():
+    import bench
+
+    wl = workloads.paper_batch(3, 200, 24)
+    rows, cu, pl, ci, st = bench.layout(wl, [(r, range(200)) for r in range(3)])
+    assert np.array_equal(rows, np.arange(wl.total_tokens))
+    assert np.array_equal(cu, wl.cu_seqlens) and np.array_equal(st, wl.item_starts)
+    rows, cu, pl, ci, st = bench.layout(wl, [(r, [i]) for r in range(3) for i in range(200)])
+    assert cu[-1] == int(sum(200 * (int(lq) + 24) for lq in wl.prefix_lens))
+    assert np.all(st == np.repeat(wl.prefix_lens, 200))
+    # the single-item layout's prefill-token ratio is Eq. 5's R(N) summed over the batch
+    assert cu[-1] / wl.total_tokens == pytest.approx(
+        sum(200 * int(lq) + 200 * 24 for lq in wl.prefix_lens) / sum(int(lq) + 200 * 24 for lq in wl.prefix_lens))

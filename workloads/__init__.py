@@ -48,6 +48,10 @@ __all__ = [
     "lm_head",
     "label_ids",
     "NAN_BF16",
+    "PAPER_QUERY_MEDIAN",
+    "PAPER_QUERY_MEAN",
+    "paper_query_lengths",
+    "paper_batch",
 ]
 
 # Quiet-NaN bit pattern in bf16 (sign 0, exponent all ones, mantissa 0x40).
@@ -212,6 +216,57 @@ def _cfg5() -> Workload:
 
 
 CONFIGS = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5}
+
+
+# --------------------------------------------------------------------------
+# the profile-labeling benchmark's shape (From Generation to Scoring, §6.1
+# "Workload": queries average 744 tokens with median 543 and 95th percentile
+# 2,047; items average 28 tokens in the chat layout, about 24 in the compact
+# readout-token layout of §3.1; 200 candidates per member)
+# --------------------------------------------------------------------------
+
+PAPER_QUERY_MEDIAN = 543
+PAPER_QUERY_MEAN = 744
+
+
+def paper_query_lengths(n: int, seed: int, stratified: bool = False) -> np.ndarray:
+    """``n`` query lengths from a lognormal with the benchmark's median and
+    mean: mu = ln(median), sigma^2 = 2 ln(mean / median) (its 95th percentile
+    is then about 2,003 tokens against the quoted 2,047), rounded to whole
+    tokens, at least 1. ``stratified``: the lognormal's quantiles at
+    (i + 0.5) / n in a seeded random order, so that a batch of a few dozen
+    members already has the distribution's median and nearly its mean (a
+    random draw of 16 from this heavy tail can miss the mean by a third)."""
+    from scipy.special import ndtri
+
+    mu = np.log(PAPER_QUERY_MEDIAN)
+    sigma = np.sqrt(2.0 * np.log(PAPER_QUERY_MEAN / PAPER_QUERY_MEDIAN))
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(len(_STREAMS))[0])
+    if stratified:
+        x = rng.permutation(np.exp(mu + sigma * ndtri((np.arange(n) + 0.5) / n)))
+    else:
+        x = rng.lognormal(mu, sigma, size=n)
+    return np.maximum(1, np.rint(x)).astype(np.int64)
+
+
+def paper_batch(num_members: int, items_per_member: int = 200, item_tokens: int = 28, *, seed: int = 6,
+                hq: int = 16, hkv: int = 8, d: int = 128, hidden: int = 1024, vocab: int = 151936,
+                num_labels: int = 2, name: str = "") -> Workload:
+    """A batch of members, each one request: a query length from
+    ``paper_query_lengths`` (stratified) and ``items_per_member`` items of ``item_tokens``
+    tokens each (28: chat layout, 24: compact layout; the count includes the
+    item's last token, where its label logits are read). The model shape
+    defaults to the single-request workload's (GQA 16/8, head_dim 128, hidden
+    1024, vocabulary 151936)."""
+    lq = paper_query_lengths(num_members, seed, stratified=True)
+    return from_lengths(
+        name or f"paper-{num_members}x{items_per_member}x{item_tokens}", lq.tolist(),
+        [[item_tokens] * items_per_member] * num_members, seed=seed, dtype="bf16", hq=hq, hkv=hkv, d=d,
+        hidden=hidden, vocab=vocab, num_labels=num_labels,
+        description=f"{num_members} members, query lengths at lognormal(median 543, mean 744) quantiles, "
+        f"{items_per_member} items of "
+        f"{item_tokens} tokens, GQA {hq}/{hkv}, head_dim {d}, bf16; scoring H={hidden} V={vocab} K={num_labels}",
+    )
 
 
 def config(k: int) -> Workload:
