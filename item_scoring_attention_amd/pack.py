@@ -9,9 +9,9 @@ requests pack one after another (variable-length batch, no attention across
 requests).
 
 The offsets ``pack_requests`` returns are exactly the host metadata that
-``mis_build_segments`` takes; ``readout_pos`` repeats what the builder
-computes (each item's closing delimiter), for callers that gather on the host.
-Pure host code: no GPU work happens here.
+``mis_build_segments`` takes; the per-token ids and each item's readout
+position (its closing delimiter) come from the builder. Pure host code: no
+GPU work happens here.
 """
 from __future__ import annotations
 
@@ -30,8 +30,7 @@ class Packed:
     cu_seqlens  [B+1] int32: packed offset of each request;
     prefix_lens [B]   int32: query length of each request;
     cu_items    [B+1] int32: global index of each request's first item;
-    item_starts [N]   int32: request-relative start of each item;
-    readout_pos [N]   int32: packed index of each item's closing delimiter.
+    item_starts [N]   int32: request-relative start of each item.
     """
 
     token_ids: np.ndarray
@@ -39,7 +38,6 @@ class Packed:
     prefix_lens: np.ndarray
     cu_items: np.ndarray
     item_starts: np.ndarray
-    readout_pos: np.ndarray
 
     @property
     def num_requests(self) -> int:
@@ -73,7 +71,7 @@ def pack_requests(requests: Sequence[Tuple[Sequence[int], Sequence[Sequence[int]
     if not (0 <= int(delimiter_id) <= np.iinfo(np.int32).max):
         raise ValueError("delimiter_id must be a token id in [0, 2^31)")
     d = np.array([delimiter_id], dtype=np.int32)
-    pieces, cu_seqlens, prefix_lens, cu_items, item_starts, readout = [], [0], [], [0], [], []
+    pieces, cu_seqlens, prefix_lens, cu_items, item_starts = [], [0], [], [0], []
     total = 0
     for r, req in enumerate(requests):
         try:
@@ -89,7 +87,6 @@ def pack_requests(requests: Sequence[Tuple[Sequence[int], Sequence[Sequence[int]
             item_starts.append(length)
             pieces += [c, d]
             length += c.size + 1
-            readout.append(total + length - 1)
         if length == 0:
             raise ValueError(f"request {r} has no query tokens and no items")
         total += length
@@ -99,8 +96,7 @@ def pack_requests(requests: Sequence[Tuple[Sequence[int], Sequence[Sequence[int]
         cu_items.append(len(item_starts))
     i32 = lambda x: np.asarray(x, dtype=np.int32)
     tokens = np.concatenate(pieces) if pieces else np.zeros(0, dtype=np.int32)
-    return Packed(tokens.astype(np.int32), i32(cu_seqlens), i32(prefix_lens), i32(cu_items), i32(item_starts),
-                  i32(readout))
+    return Packed(tokens.astype(np.int32), i32(cu_seqlens), i32(prefix_lens), i32(cu_items), i32(item_starts))
 
 
 def build_packed_segments(packed: Packed, block_m: int, block_n: int, dev_buf=None, stream=None):

@@ -120,8 +120,10 @@ def test_packed_batch_builds_the_packers_readout_positions():
             for _ in range(6)]
     p = pack_requests(reqs, delimiter_id=50001)
     seg = build_packed_segments(p, 64, 64)
-    assert np.array_equal(host(seg.array("readout_pos")), p.readout_pos)
     so = oracle.build_segments(p.cu_seqlens, p.prefix_lens, p.cu_items, p.item_starts)
+    readout = host(seg.array("readout_pos"))
+    assert np.array_equal(readout, so["readout_pos"])
+    assert (p.token_ids[readout] == 50001).all()  # every item is read at its delimiter
     assert np.array_equal(host(seg.array("item_id")), so["item_id"])
     assert np.array_equal(host(seg.array("pos_id")), so["pos_id"])
 

@@ -16,8 +16,10 @@ def test_hand_worked_example():
     assert p.prefix_lens.tolist() == [3]
     assert p.cu_items.tolist() == [0, 3]
     assert p.item_starts.tolist() == [3, 6, 8]
-    assert p.readout_pos.tolist() == [5, 7, 8]
-    for a in (p.token_ids, p.cu_seqlens, p.prefix_lens, p.cu_items, p.item_starts, p.readout_pos):
+    # each item is read at its closing delimiter (the oracle's readout rule)
+    seg = oracle.build_segments(p.cu_seqlens, p.prefix_lens, p.cu_items, p.item_starts)
+    assert seg["readout_pos"].tolist() == [5, 7, 8]
+    for a in (p.token_ids, p.cu_seqlens, p.prefix_lens, p.cu_items, p.item_starts):
         assert a.dtype == np.int32
 
 
@@ -28,7 +30,8 @@ def test_requests_pack_one_after_another():
     assert p.prefix_lens.tolist() == [1, 2, 1]
     assert p.cu_items.tolist() == [0, 1, 1, 3]
     assert p.item_starts.tolist() == [1, 1, 3]        # request-relative
-    assert p.readout_pos.tolist() == [3, 8, 12]       # packed
+    seg = oracle.build_segments(p.cu_seqlens, p.prefix_lens, p.cu_items, p.item_starts)
+    assert seg["readout_pos"].tolist() == [3, 8, 12]  # packed
     assert p.num_requests == 3 and p.total_items == 3
 
 
@@ -41,8 +44,7 @@ def test_offsets_agree_with_the_oracle_segments():
         reqs.append((q, items))
     p = pack_requests(reqs, delimiter_id=1001)
     seg = oracle.build_segments(p.cu_seqlens, p.prefix_lens, p.cu_items, p.item_starts)
-    assert np.array_equal(seg["readout_pos"], p.readout_pos)
-    assert (p.token_ids[p.readout_pos] == 1001).all()
+    assert (p.token_ids[seg["readout_pos"]] == 1001).all()
     # every item's tokens, then its delimiter, sit at its segment in order
     n = 0
     for r, (q, items) in enumerate(reqs):
