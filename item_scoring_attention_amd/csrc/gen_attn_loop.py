@@ -132,6 +132,7 @@ MFMA_RS = "v_mfma_f32_16x16x32_bf16"  # row sums (half the cycles of MFMA)
 # VALU 4) and before the first one (while the first K fragment arrives).
 SLOT_BUDGET = 24
 HEAD_BUDGET = 16
+EXP_COST = 10  # issue cycles charged for a v_exp_f32 in that budget
 
 
 def vr(a, n=1):
@@ -199,8 +200,8 @@ def softmax_graph(s_cur: int, p_cur: int, c: str):
         war = done_pair.get(i - NPT, ())
         fa = add(f"v_fma_f32 {vr(ea)}, {vr(sa)}, {c}, -{vr(m)}", 4, war)
         fb = add(f"v_fma_f32 {vr(eb)}, {vr(sa + 1)}, {c}, -{vr(m)}", 4, war)
-        xa = add(f"v_exp_f32 {vr(ea)}, {vr(ea)}", 10, [fa])
-        xb = add(f"v_exp_f32 {vr(eb)}, {vr(eb)}", 10, [fb])
+        xa = add(f"v_exp_f32 {vr(ea)}, {vr(ea)}", EXP_COST, [fa])
+        xb = add(f"v_exp_f32 {vr(eb)}, {vr(eb)}", EXP_COST, [fb])
         cv = add(f"v_cvt_pk_bf16_f32 {vr(p_cur + 8 * qb + pi)}, {vr(ea)}, {vr(eb)}", 4, [xa, xb])
         lm = last_max[qb]
         mx = add(f"v_max_f32 {vr(VMX[qb])}, {vr(ea)}, {vr(eb)}" if lm is None else
