@@ -320,8 +320,9 @@ def percentiles(xs) -> dict:
             "n": int(a.size)}
 
 
-def mfma_peak_tflops(stream) -> float:
-    """Best bf16 MFMA rate of three launches of the probe kernel (TFLOP/s)."""
+def mfma_peak_tflops(stream) -> dict:
+    """Best bf16 MFMA rate of four launches of the probe kernel (TFLOP/s), with
+    small repeating operands and with random N(0, 1)-like operands."""
     import ctypes
 
     import torch
@@ -330,24 +331,27 @@ def mfma_peak_tflops(stream) -> float:
 
     lib = ctypes.CDLL(B.PROBE_LIB)
     lib.mis_probe_mfma_bf16.restype = ctypes.c_int
-    lib.mis_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mis_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.mis_probe_mfma_bf16_flops.restype = ctypes.c_double
     lib.mis_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     blocks, iters = 2048, 4096
     sink = torch.empty(blocks, dtype=torch.float32, device="cuda")
-    best = 0.0
-    for _ in range(4):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        rc = lib.mis_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(sink.data_ptr()),
-                                     ctypes.c_void_p(stream.cuda_stream))
-        if rc != 0:
-            raise RuntimeError(f"MFMA probe launch failed: hip error {rc}")
-        b.record(stream)
-        b.synchronize()
-        best = max(best, lib.mis_probe_mfma_bf16_flops(blocks, iters) / (a.elapsed_time(b) * 1e-3) / 1e12)
-    return best
+    out = {}
+    for mode, name in ((0, "repeating_operands"), (1, "random_operands")):
+        best = 0.0
+        for _ in range(4):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = lib.mis_probe_mfma_bf16(blocks, iters, mode, ctypes.c_void_p(sink.data_ptr()),
+                                         ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"MFMA probe launch failed: hip error {rc}")
+            b.record(stream)
+            b.synchronize()
+            best = max(best, lib.mis_probe_mfma_bf16_flops(blocks, iters) / (a.elapsed_time(b) * 1e-3) / 1e12)
+        out[name] = round(best, 1)
+    return out
 
 
 def main(argv=None):
@@ -538,8 +542,8 @@ def main(argv=None):
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "algorithmic_flops_per_launch": flops,
-            "measured_mfma_peak": round(mfma_peak, 1),
-            "frac_of_measured_peak": round(tflops / mfma_peak, 4),
+            "measured_mfma_peak": mfma_peak,
+            "frac_of_measured_peak": {k: round(tflops / p, 4) for k, p in mfma_peak.items()},
             "duration_ms": {"mean": round(t_att, 4), "median": kernel_stats["warm"]["attention"]["median"]},
         },
     }
