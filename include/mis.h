@@ -284,7 +284,9 @@ int mis_score_labels_at(const int32_t *positions_h, int32_t num_rows, int32_t nu
  * unless a choice is set here; the setting holds for later calls on the same
  * thread until changed, and other threads are not affected.
  *   attention: NULL, "" or "auto" (by shape); "pipe" (pipelined loop, 64 query
- *              rows per wave); "pipe32" (pipelined loop, 32 rows per wave);
+ *              rows per wave, 4 heads per workgroup when the GQA group size is a
+ *              multiple of 4, else 2); "pipe2" (the same loop, 2 heads per
+ *              workgroup); "pipe32" (pipelined loop, 32 rows per wave);
  *              "classic" (plain loop). The pipelined loops need an even GQA
  *              group size: odd group sizes always take the plain loop.
  *   score:     NULL, "" or "auto"; "narrow" (128 vocabulary rows x up to 128

@@ -587,7 +587,8 @@ int mis_set_kernel_choice(const char *attention, const char *score) {
   else if (!std::strcmp(attention, "pipe")) af = mis::AttnForce::Pipe;
   else if (!std::strcmp(attention, "pipe32")) af = mis::AttnForce::Pipe32;
   else if (!std::strcmp(attention, "classic")) af = mis::AttnForce::Classic;
-  else return fail(MIS_ERR_ARG, "unknown attention kernel choice '%s' (auto, pipe, pipe32, classic)", attention);
+  else if (!std::strcmp(attention, "pipe2")) af = mis::AttnForce::Pipe2;
+  else return fail(MIS_ERR_ARG, "unknown attention kernel choice '%s' (auto, pipe, pipe2, pipe32, classic)", attention);
   mis::ScoreForce sf;
   int ni = 0;
   if (!score || !*score || !std::strcmp(score, "auto")) sf = mis::ScoreForce::Auto;

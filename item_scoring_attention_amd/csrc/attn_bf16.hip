@@ -443,19 +443,26 @@ AttnKernel pick_attention_bf16(const mis_segments &seg, int hq, int hkv, AttnFor
   if (gsz % 2 != 0) return AttnKernel::Classic1;
   switch (force) {
     case AttnForce::Pipe: return gsz % 4 == 0 ? AttnKernel::Pipe4 : AttnKernel::Pipe2;
+    case AttnForce::Pipe2: return AttnKernel::Pipe2;
     case AttnForce::Pipe32: return AttnKernel::Pipe32;
     case AttnForce::Classic: return AttnKernel::Classic2;
     case AttnForce::Auto: break;
   }
-  // Long runs of work (GQA groups of 4 or more, query tiles that visit 48
-  // key tiles or more on average, and at least 8 four-head workgroups per
-  // CU) take the pipelined loop with 64 query rows per wave: one wave per
-  // SIMD, so it cannot hide the fixed cost of starting a query tile behind
-  // another workgroup, but its loop is the fastest. Other shapes take the
-  // pipelined loop with 32 rows per wave, two waves per SIMD.
-  const bool long_runs = gsz % 4 == 0 && int64_t(seg.num_visits) >= 48 * int64_t(seg.num_work) &&
-                         int64_t(seg.num_work) * (hq / 4) >= 8 * int64_t(device_cus());
-  return long_runs ? AttnKernel::Pipe4 : AttnKernel::Pipe32;
+  // The loop with 64 query rows per wave reads half the LDS per MFMA of the
+  // 32-row loop, but runs one wave per SIMD, so it cannot hide the fixed
+  // cost of starting a query tile behind another workgroup. Measured on the
+  // workloads here: GQA groups of 4 or more take it with 4 heads per
+  // workgroup when query tiles visit 48 key tiles or more on average and
+  // every CU gets at least 8 such workgroups (the long-prefix batch); groups
+  // of 2 (or 6, 10, ...) take it with 2 heads per workgroup from 20 visits
+  // per query tile on (2048- to 8192-token prefixes with 64 items: 3-7%
+  // faster; shorter prefixes and the profile-labeling batch: 4-8% slower).
+  // Other shapes take the 32-row loop, two waves per SIMD.
+  const int64_t visits = seg.num_visits, tiles = seg.num_work;
+  if (gsz % 4 == 0 && visits >= 48 * tiles && tiles * (hq / 4) >= 8 * int64_t(device_cus()))
+    return AttnKernel::Pipe4;
+  if (gsz % 4 == 2 && visits >= 20 * tiles) return AttnKernel::Pipe2;
+  return AttnKernel::Pipe32;
 }
 
 const char *attention_bf16_name(AttnKernel k) {
@@ -479,8 +486,8 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
   const __bf16 *vp = static_cast<const __bf16 *>(v);
   __bf16 *op = static_cast<__bf16 *>(o);
   switch (kernel) {
-    case AttnKernel::Pipe4:
-    case AttnKernel::Pipe2: return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, st);
+    case AttnKernel::Pipe4: return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, 4, st);
+    case AttnKernel::Pipe2: return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, 2, st);
     case AttnKernel::Pipe32: return launch_attention_bf16_pipe32(seg, q, k, v, o, hq, hkv, scale, items_only, st);
     case AttnKernel::Classic2: return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
     case AttnKernel::Classic1: return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);

@@ -391,13 +391,13 @@ hipError_t launch_pipe(const mis_segments &seg, const void *q, const void *k, co
 }  // namespace
 
 hipError_t launch_attention_bf16_pipe(const mis_segments &seg, const void *q, const void *k, const void *v, void *o,
-                                      int hq, int hkv, float scale, int items_only, hipStream_t st) {
+                                      int hq, int hkv, float scale, int items_only, int heads, hipStream_t st) {
   const int gsz = hq / hkv;
-  if (gsz % 2 != 0) return hipErrorInvalidValue;
+  if (gsz % heads != 0 || (heads != 2 && heads != 4)) return hipErrorInvalidValue;
   const float c = scale * kLog2e;
   // 4 heads per workgroup share each staged K/V tile among 4 waves (one
-  // workgroup per CU, a 3-stage ring); 2 heads run two workgroups per CU.
-  if (gsz % 4 == 0) return launch_pipe<4, 1>(seg, q, k, v, o, hq, hkv, c, items_only, st);
+  // workgroup per CU, a 4-stage ring); 2 heads run two workgroups per CU.
+  if (heads == 4) return launch_pipe<4, 1>(seg, q, k, v, o, hq, hkv, c, items_only, st);
   return launch_pipe<2, 1>(seg, q, k, v, o, hq, hkv, c, items_only, st);
 }
 

@@ -60,7 +60,7 @@ enum class AttnKernel : int {
   Classic1 = 4, // attn_dma_kernel<2, 1>: plain loop, 1 head x 2 row blocks (odd group sizes)
 };
 // A caller's forced choice (tests, A/B comparisons); Auto = by shape.
-enum class AttnForce : int { Auto = 0, Pipe = 1, Pipe32 = 2, Classic = 3 };
+enum class AttnForce : int { Auto = 0, Pipe = 1, Pipe32 = 2, Classic = 3, Pipe2 = 4 };
 AttnKernel pick_attention_bf16(const mis_segments &seg, int hq, int hkv, AttnForce force);
 const char *attention_bf16_name(AttnKernel k);
 
@@ -68,11 +68,12 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
                                  const void *v, void *o, int hq, int hkv, int d, float scale,
                                  int items_only, AttnKernel kernel, hipStream_t stream);
 
-// 64 query rows per wave, software-pipelined key-tile loop (even GQA group
-// sizes, head_dim 128); launch_attention_bf16 dispatches to it.
+// 64 query rows per wave, software-pipelined key-tile loop, `heads` (2 or 4,
+// dividing the GQA group) query heads per workgroup, head_dim 128;
+// launch_attention_bf16 dispatches to it.
 hipError_t launch_attention_bf16_pipe(const mis_segments &seg, const void *q, const void *k,
                                       const void *v, void *o, int hq, int hkv, float scale,
-                                      int items_only, hipStream_t stream);
+                                      int items_only, int heads, hipStream_t stream);
 
 // The same loop with 32 query rows per wave, two waves per SIMD (even GQA
 // group sizes, head_dim 128).

@@ -263,15 +263,22 @@ def test_kernel_choice_names_and_rejects_unknown():
                                            num_work=1808, num_visits=1808 * 259), None)
         mis.set_kernel_choice()
         assert mis.attention_kernel_name(seg, bf16, 64, 8, 128) == "attn_pipe_kernel<4, 1>"
-        assert mis.attention_kernel_name(seg, bf16, 16, 8, 128) == "attn_pipe_kernel<2, 2>"
+        assert mis.attention_kernel_name(seg, bf16, 16, 8, 128) == "attn_pipe_kernel<2, 1>"
         assert mis.attention_kernel_name(seg, bf16, 12, 4, 128) == "attn_dma_kernel<2, 1>"
         assert mis.attention_kernel_name(seg, mis.MIS_F32, 4, 4, 64) == "attn_f32_kernel"
         short = mis.Segments(mis.MisSegments(num_requests=1, total_tokens=4160, block_m=64, block_n=64,
                                              num_work=65, num_visits=65 * 20), None)
         assert mis.attention_kernel_name(short, bf16, 64, 8, 128) == "attn_pipe_kernel<2, 2>"
+        # groups of 2: 64 rows per wave from 20 visits per query tile on
+        assert mis.attention_kernel_name(short, bf16, 16, 8, 128) == "attn_pipe_kernel<2, 1>"
+        few = mis.Segments(mis.MisSegments(num_requests=1, total_tokens=4160, block_m=64, block_n=64,
+                                           num_work=65, num_visits=65 * 20 - 1), None)
+        assert mis.attention_kernel_name(few, bf16, 16, 8, 128) == "attn_pipe_kernel<2, 2>"
         mis.set_kernel_choice(attention="pipe")
         assert mis.attention_kernel_name(short, bf16, 16, 8, 128) == "attn_pipe_kernel<2, 1>"
         assert mis.attention_kernel_name(short, bf16, 12, 4, 128) == "attn_dma_kernel<2, 1>"
+        mis.set_kernel_choice(attention="pipe2")
+        assert mis.attention_kernel_name(short, bf16, 64, 8, 128) == "attn_pipe_kernel<2, 1>"
         mis.set_kernel_choice(attention="classic")
         assert mis.attention_kernel_name(short, bf16, 64, 8, 128) == "attn_dma_kernel<2, 2>"
         with pytest.raises(ValueError):

@@ -20,7 +20,7 @@ from gpu_common import (TOL_BF16_ATTN, TOL_F32, attention, build, cached, host, 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(autouse=True, params=["auto", "pipe", "pipe32", "classic"])
+@pytest.fixture(autouse=True, params=["auto", "pipe", "pipe2", "pipe32", "classic"])
 def attention_kernel(request):
     """Run every case with the bf16 kernel chosen by shape, and forced to each
     of the three kernels (the pipelined loop with 64 or with 32 query rows per

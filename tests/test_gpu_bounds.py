@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 PAD = 64
 
 
-@pytest.fixture(autouse=True, params=["auto", "pipe", "pipe32", "classic"])
+@pytest.fixture(autouse=True, params=["auto", "pipe", "pipe2", "pipe32", "classic"])
 def attention_kernel(request):
     """Each bf16 attention kernel, forced, and the one chosen by shape."""
     mis.set_kernel_choice(attention=request.param)
