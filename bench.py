@@ -23,6 +23,7 @@ the whole step time.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -269,11 +270,14 @@ def paper(args) -> int:
         for _ in range(2):
             step()
         torch.cuda.synchronize()
+        gc.collect()
+        gc.disable()
         t0 = time.perf_counter()
         for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        gc.enable()
         lens = np.diff(cu)
         pairs = int(sum(int(a) * (int(a) + 1) // 2 for a in pl))
         for r in range(len(pl)):
@@ -452,12 +456,17 @@ def main(argv=None):
     # Timed region: K steps back to back, HIP events on the launch stream
     # around every call (each event adds a few microseconds of queue time to
     # the step, negligible against the long-prefix step's ~40 ms).
+    # (the Python garbage collector is held off meanwhile: a collection pass
+    # on the host can stall the launches of one step by milliseconds)
     warm = []
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(warm)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
     def split(marks):
@@ -475,7 +484,9 @@ def main(argv=None):
             step(cold)
         torch.cuda.synchronize()
         cold_ms = split(cold)
-    print("[bench] timed; measuring the MFMA probe and the rotary kernel", file=sys.stderr, flush=True)
+    print("[bench] timed; measuring the MFMA probe and the rotary kernels", file=sys.stderr, flush=True)
+    t_att_warm = float(np.mean(warm_ms["attention"]))
+    rope_tab = torch.empty((seg.max_seqlen, wl.d), dtype=torch.float32, device="cuda")
     mfma_peak = mfma_peak_tflops(stream)
 
     # Rotary embedding at the reused positions (in place on q and k; not in
@@ -493,6 +504,17 @@ def main(argv=None):
 
     t_rope = back_to_back(lambda: mis.mis_apply_rope(seg, qd, kd, 1e6, stream=stream), 10)
     rope_bytes = 2 * wl.total_tokens * (wl.hq + wl.hkv) * wl.d * 2  # read and write q, k (bf16)
+    # The same rotation with Q turned inside the attention kernel: K alone in
+    # the pass, Q from the cos/sin table as it is loaded (outputs bit-identical
+    # to pass + attention). The table depends on theta, D and the longest
+    # request only (built once, for every layer and batch).
+    n_att = max(2, min(20, int(200.0 / max(t_att_warm, 1e-3))))
+    t_table = back_to_back(lambda: mis.mis_rope_table(seg.max_seqlen, wl.d, 1e6, table=rope_tab, stream=stream), 3)
+    t_rope_k = back_to_back(lambda: mis.mis_apply_rope(seg, None, kd, 1e6, stream=stream), 10)
+    t_att_plain = back_to_back(lambda: mis.mis_attention_prefill(seg, qd, kd, vd, o=od, stream=stream), n_att)
+    t_att_fused = back_to_back(lambda: mis.mis_attention_prefill_rope(seg, qd, kd, vd, rope_tab, o=od,
+                                                                      stream=stream), n_att)
+    rope_k_bytes = 2 * wl.total_tokens * wl.hkv * wl.d * 2
 
     flops = attention_flops(wl)
     t_att = float(np.mean(warm_ms["attention"]))
@@ -569,6 +591,19 @@ def main(argv=None):
         "peak_gbs": PEAK_HBM_GBS,
         "frac": round(rope_bytes / (t_rope * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "algorithmic_bytes_per_launch": rope_bytes,
+        "k_only": {"ms": round(t_rope_k, 4), "algorithmic_bytes_per_launch": rope_k_bytes,
+                   "achieved_gbs": round(rope_k_bytes / (t_rope_k * 1e-3) / 1e9, 1)},
+    }
+    # attention with the rotation, both ways (back-to-back launches, same state)
+    out["rope_step_ms"] = {
+        "separate": round(t_rope + t_att_plain, 4),
+        "fused": round(t_rope_k + t_att_fused, 4),
+        "rotation_pass_q_and_k": round(t_rope, 4),
+        "rotation_pass_k": round(t_rope_k, 4),
+        "attention": round(t_att_plain, 4),
+        "attention_rotating_q": round(t_att_fused, 4),
+        "table_once": round(t_table, 4),
+        "table_positions": int(seg.max_seqlen),
     }
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB

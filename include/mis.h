@@ -194,11 +194,52 @@ int mis_attention_append(const mis_segments *seg, const void *q, const void *k, 
  *
  * q [T, hq, D] and k [T, hkv, D]: device, token-major, contiguous, element
  * type dt, rewritten in place (call once per batch, before
- * mis_attention_prefill). D must be 64 or 128; theta > 0 (for example 10000
- * or 1000000). Errors: ARG, UNSUPPORTED, HIP.
+ * mis_attention_prefill). q may be NULL: then only K is rotated (for the
+ * *_rope attention calls, which rotate Q themselves). D must be 64 or 128;
+ * theta > 0 (for example 10000 or 1000000). Errors: ARG, UNSUPPORTED, HIP.
  */
 int mis_apply_rope(const mis_segments *seg, void *q, void *k, mis_dtype dt, int32_t hq, int32_t hkv,
                    int32_t head_dim, float theta, void *stream);
+
+/*
+ * Device bytes of a rotary table for num_positions positions:
+ * num_positions x head_dim/2 x 2 floats. Errors: ARG, UNSUPPORTED.
+ */
+int mis_rope_table_bytes(int32_t num_positions, int32_t head_dim, size_t *bytes);
+
+/*
+ * Rotary table for the attention calls that rotate Q while loading it:
+ * table[p][i] = (cos, sin) of p * theta^(-2i/D) for p < num_positions and
+ * i < D/2, float32 pairs, the same values the rotation of mis_apply_rope
+ * computes (same position-id rule: From Generation to Scoring, §4.1). It
+ * depends on theta, D and num_positions only, so one table serves every
+ * layer and every batch whose position ids stay below num_positions.
+ *
+ * table: device, at least mis_rope_table_bytes; written on stream. D must be
+ * 64 or 128; theta > 0. Errors: ARG, UNSUPPORTED, HIP.
+ */
+int mis_rope_table(int32_t num_positions, int32_t head_dim, float theta, void *table, size_t table_bytes,
+                   void *stream);
+
+/*
+ * mis_attention_prefill and mis_attention_append with the rotary embedding of
+ * Q applied inside the kernel as Q is loaded: q holds Q before rotation and
+ * is not modified; k must already be rotated (mis_apply_rope with q = NULL).
+ * The result equals mis_apply_rope on Q and K followed by
+ * mis_attention_prefill (or _append), bit for bit, without the pass over Q.
+ * rope_table: from mis_rope_table for the same D, with table_positions
+ * (its num_positions) >= seg->max_seqlen, so every position id is inside.
+ * bf16 only. Other arguments, layout and errors as for mis_attention_prefill;
+ * ARG for a missing or short table, UNSUPPORTED for f32.
+ */
+int mis_attention_prefill_rope(const mis_segments *seg, const void *q, const void *k, const void *v,
+                               void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                               float softmax_scale, const void *rope_table, int32_t table_positions,
+                               void *stream);
+int mis_attention_append_rope(const mis_segments *seg, const void *q, const void *k, const void *v,
+                              void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                              float softmax_scale, const void *rope_table, int32_t table_positions,
+                              void *stream);
 
 /*
  * Device workspace bytes of mis_score_labels for N items, vocabulary V,

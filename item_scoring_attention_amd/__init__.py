@@ -8,6 +8,9 @@ The computation lives in ``libmis.so`` (HIP kernels behind the C ABI of
 * ``mis_apply_rope``: rotary embedding of Q and K at the reused positions;
 * ``mis_attention_prefill``: MIS prefill attention on bf16 MFMA (or fp32);
   ``mis_attention_append``: the same for item rows only, against a cached prefix;
+  ``mis_attention_prefill_rope`` / ``mis_attention_append_rope``: the same with
+  Q rotated inside the kernel from a ``mis_rope_table`` (K rotated beforehand
+  by ``mis_apply_rope`` with ``q=None``);
 * ``mis_score_labels``: readout gather, LM-head contraction and full-vocab
   logsumexp, writing one label-score row per item (``mis_score_labels_at``:
   at any token rows, e.g. several readout markers per item;
@@ -40,9 +43,13 @@ from ._lib import (  # noqa: F401
     load,
     mis_apply_rope,
     mis_attention_append,
+    mis_attention_append_rope,
     mis_attention_prefill,
+    mis_attention_prefill_rope,
     mis_attention_tile_shape,
     mis_build_segments,
+    mis_rope_table,
+    mis_rope_table_bytes,
     mis_score_labels,
     mis_score_labels_at,
     mis_score_labels_noalloc,

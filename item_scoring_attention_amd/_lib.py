@@ -89,6 +89,17 @@ SIGNATURES = {
     "mis_apply_rope": (ctypes.c_int, [ctypes.POINTER(MisSegments), ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_float, ctypes.c_void_p]),
+    "mis_rope_table_bytes": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
+    "mis_rope_table": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]),
+    "mis_attention_prefill_rope": (ctypes.c_int, [ctypes.POINTER(MisSegments), ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                                  ctypes.c_int32, ctypes.c_void_p]),
+    "mis_attention_append_rope": (ctypes.c_int, [ctypes.POINTER(MisSegments), ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
+                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                                 ctypes.c_int32, ctypes.c_void_p]),
     "mis_score_workspace_bytes": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32, ctypes.c_int,
                                                  ctypes.POINTER(ctypes.c_size_t)]),
@@ -330,7 +341,21 @@ def mis_attention_append(seg: Segments, q, k, v, o, softmax_scale: float = 0.0, 
     return _attention("mis_attention_append", seg, q, k, v, o, softmax_scale, stream)
 
 
-def _attention(fn: str, seg: Segments, q, k, v, o, softmax_scale: float, stream):
+def mis_attention_prefill_rope(seg: Segments, q, k, v, rope_table, o=None, softmax_scale: float = 0.0,
+                               stream=None):
+    """``mis_attention_prefill`` with Q rotated inside the kernel: q is Q before
+    rotation (left unchanged), k already rotated, rope_table from
+    ``mis_rope_table`` with at least ``seg.max_seqlen`` positions."""
+    return _attention("mis_attention_prefill_rope", seg, q, k, v, o, softmax_scale, stream, rope_table)
+
+
+def mis_attention_append_rope(seg: Segments, q, k, v, o, rope_table, softmax_scale: float = 0.0, stream=None):
+    """``mis_attention_append`` with Q rotated inside the kernel (see
+    ``mis_attention_prefill_rope``)."""
+    return _attention("mis_attention_append_rope", seg, q, k, v, o, softmax_scale, stream, rope_table)
+
+
+def _attention(fn: str, seg: Segments, q, k, v, o, softmax_scale: float, stream, rope_table=None):
     torch = _torch()
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be [T, heads, D]")
@@ -344,26 +369,53 @@ def _attention(fn: str, seg: Segments, q, k, v, o, softmax_scale: float, stream)
         o = torch.empty_like(q)
     elif o.shape != q.shape or o.dtype != q.dtype:
         raise ValueError("o must match q in shape and dtype")
-    _check(getattr(load(), fn)(ctypes.byref(seg.struct), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
-                               _dev(o, "o"), _dtype_code(q), q.shape[1], k.shape[1], q.shape[2],
-                               float(softmax_scale), _stream(stream)))
+    args = [ctypes.byref(seg.struct), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dtype_code(q),
+            q.shape[1], k.shape[1], q.shape[2], float(softmax_scale)]
+    if rope_table is not None:
+        if rope_table.dtype != torch.float32 or rope_table.dim() != 2 or rope_table.shape[1] != q.shape[2]:
+            raise ValueError("rope_table must be float32 [positions, head_dim] from mis_rope_table")
+        args += [_dev(rope_table, "rope_table"), rope_table.shape[0]]
+    _check(getattr(load(), fn)(*args, _stream(stream)))
     return o
 
 
 def mis_apply_rope(seg: Segments, q, k, theta: float, stream=None):
     """Rotary embedding of q ``[T,Hq,D]`` and k ``[T,Hkv,D]`` in place at the
-    segment position ids; returns (q, k)."""
-    if q.dim() != 3 or k.dim() != 3:
+    segment position ids; returns (q, k). ``q=None`` rotates k alone (for the
+    ``*_rope`` attention calls, which rotate Q themselves)."""
+    if (q is not None and q.dim() != 3) or k.dim() != 3:
         raise ValueError("q and k must be [T, heads, D]")
-    if q.dtype != k.dtype:
+    if q is not None and q.dtype != k.dtype:
         raise ValueError("q and k must have the same dtype")
-    if q.shape[0] != seg.total_tokens or k.shape[0] != seg.total_tokens:
+    if k.shape[0] != seg.total_tokens or (q is not None and q.shape[0] != seg.total_tokens):
         raise ValueError("token count of q/k differs from the segments")
-    if q.shape[2] != k.shape[2]:
+    if q is not None and q.shape[2] != k.shape[2]:
         raise ValueError("head_dim of q and k differ")
-    _check(load().mis_apply_rope(ctypes.byref(seg.struct), _dev(q, "q"), _dev(k, "k"), _dtype_code(q),
-                                 q.shape[1], k.shape[1], q.shape[2], float(theta), _stream(stream)))
+    hq = q.shape[1] if q is not None else k.shape[1]
+    _check(load().mis_apply_rope(ctypes.byref(seg.struct), _dev(q, "q") if q is not None else None, _dev(k, "k"),
+                                 _dtype_code(k), hq, k.shape[1], k.shape[2], float(theta), _stream(stream)))
     return q, k
+
+
+def mis_rope_table_bytes(num_positions: int, head_dim: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().mis_rope_table_bytes(int(num_positions), int(head_dim), ctypes.byref(out)))
+    return out.value
+
+
+def mis_rope_table(num_positions: int, head_dim: int, theta: float, table=None, device=None, stream=None):
+    """Rotary table float32 ``[num_positions, head_dim]``: (cos, sin) of pair i
+    of position p at ``[p, 2i]``, ``[p, 2i+1]``; see ``include/mis.h``."""
+    torch = _torch()
+    nbytes = mis_rope_table_bytes(num_positions, head_dim)
+    if table is None:
+        table = torch.empty((int(num_positions), int(head_dim)), dtype=torch.float32,
+                            device=device if device is not None else "cuda")
+    elif table.dtype != torch.float32 or table.numel() * 4 < nbytes:
+        raise ValueError("table must be float32 with at least num_positions x head_dim elements")
+    _check(load().mis_rope_table(int(num_positions), int(head_dim), float(theta), _dev(table, "table"),
+                                 table.numel() * 4, _stream(stream)))
+    return table
 
 
 # ---------------------------------------------------------------- scoring

@@ -379,9 +379,18 @@ int mis_attention_tile_shape(mis_dtype dt, int32_t hq, int32_t hkv, int32_t head
 
 namespace {
 
+// Inverse frequencies theta^(-2i/D) of the rotary embedding, i < D/2.
+mis::RopeFreq rope_freq(float theta, int head_dim) {
+  mis::RopeFreq f{};
+  for (int i = 0; i < head_dim / 2; ++i) f.inv[i] = std::pow(double(theta), -2.0 * i / head_dim);
+  return f;
+}
+
+// rope_table: NULL, or the rotary table of table_positions positions (Q is
+// then rotated inside the kernel).
 int attention_call(const mis_segments *seg, const void *q, const void *k, const void *v, void *o,
                    mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim, float softmax_scale,
-                   int items_only, void *stream) {
+                   int items_only, const void *rope_table, int32_t table_positions, void *stream) {
   if (!seg) return fail(MIS_ERR_ARG, "seg is NULL");
   if (!q || !k || !v || !o) return fail(MIS_ERR_ARG, "q, k, v and o must be non-NULL");
   int32_t bm, bn;
@@ -393,6 +402,12 @@ int attention_call(const mis_segments *seg, const void *q, const void *k, const 
   if (seg->total_tokens < 1 || !seg->work || !seg->tile_class || !seg->item_id)
     return fail(MIS_ERR_ARG, "seg is not a built segment descriptor");
   if (!std::isfinite(softmax_scale)) return fail(MIS_ERR_ARG, "softmax_scale is not finite");
+  if (rope_table) {
+    if (dt != MIS_BF16) return fail(MIS_ERR_UNSUPPORTED, "Q rotation inside attention is bf16 only");
+    if (table_positions < seg->max_seqlen)
+      return fail(MIS_ERR_ARG, "rotary table of %d positions is short: requests reach %d tokens", table_positions,
+                  seg->max_seqlen);
+  }
   // The bf16 kernels address a request's Q, K and V rows with 32-bit byte
   // offsets from the request start (up to the end of its last 64-row tile).
   if (dt == MIS_BF16 &&
@@ -405,7 +420,8 @@ int attention_call(const mis_segments *seg, const void *q, const void *k, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = dt == MIS_BF16
                      ? mis::launch_attention_bf16(*seg, q, k, v, o, hq, hkv, head_dim, scale, items_only,
-                                                  mis::pick_attention_bf16(*seg, hq, hkv, g_attn_force), st)
+                                                  mis::pick_attention_bf16(*seg, hq, hkv, g_attn_force),
+                                                  static_cast<const float *>(rope_table), st)
                      : mis::launch_attention_f32(*seg, static_cast<const float *>(q),
                                                  static_cast<const float *>(k),
                                                  static_cast<const float *>(v), static_cast<float *>(o),
@@ -419,19 +435,37 @@ int attention_call(const mis_segments *seg, const void *q, const void *k, const 
 int mis_attention_prefill(const mis_segments *seg, const void *q, const void *k, const void *v,
                           void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
                           float softmax_scale, void *stream) {
-  return attention_call(seg, q, k, v, o, dt, hq, hkv, head_dim, softmax_scale, 0, stream);
+  return attention_call(seg, q, k, v, o, dt, hq, hkv, head_dim, softmax_scale, 0, nullptr, 0, stream);
 }
 
 int mis_attention_append(const mis_segments *seg, const void *q, const void *k, const void *v,
                          void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
                          float softmax_scale, void *stream) {
-  return attention_call(seg, q, k, v, o, dt, hq, hkv, head_dim, softmax_scale, 1, stream);
+  return attention_call(seg, q, k, v, o, dt, hq, hkv, head_dim, softmax_scale, 1, nullptr, 0, stream);
+}
+
+int mis_attention_prefill_rope(const mis_segments *seg, const void *q, const void *k, const void *v,
+                               void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                               float softmax_scale, const void *rope_table, int32_t table_positions,
+                               void *stream) {
+  if (!rope_table) return fail(MIS_ERR_ARG, "rope_table is NULL");
+  return attention_call(seg, q, k, v, o, dt, hq, hkv, head_dim, softmax_scale, 0, rope_table, table_positions,
+                        stream);
+}
+
+int mis_attention_append_rope(const mis_segments *seg, const void *q, const void *k, const void *v,
+                              void *o, mis_dtype dt, int32_t hq, int32_t hkv, int32_t head_dim,
+                              float softmax_scale, const void *rope_table, int32_t table_positions,
+                              void *stream) {
+  if (!rope_table) return fail(MIS_ERR_ARG, "rope_table is NULL");
+  return attention_call(seg, q, k, v, o, dt, hq, hkv, head_dim, softmax_scale, 1, rope_table, table_positions,
+                        stream);
 }
 
 int mis_apply_rope(const mis_segments *seg, void *q, void *k, mis_dtype dt, int32_t hq, int32_t hkv,
                    int32_t head_dim, float theta, void *stream) {
   if (!seg) return fail(MIS_ERR_ARG, "seg is NULL");
-  if (!q || !k) return fail(MIS_ERR_ARG, "q and k must be non-NULL");
+  if (!k) return fail(MIS_ERR_ARG, "k must be non-NULL");
   if (hq < 1 || hkv < 1 || hq % hkv)
     return fail(MIS_ERR_ARG, "need hq >= 1, hkv >= 1 and hq %% hkv == 0 (got %d, %d)", hq, hkv);
   if (head_dim != 64 && head_dim != 128)
@@ -439,10 +473,34 @@ int mis_apply_rope(const mis_segments *seg, void *q, void *k, mis_dtype dt, int3
   if (dt != MIS_F32 && dt != MIS_BF16) return fail(MIS_ERR_UNSUPPORTED, "unknown dtype %d", int(dt));
   if (!(theta > 0.f) || !std::isfinite(theta)) return fail(MIS_ERR_ARG, "theta must be a positive finite number");
   if (seg->total_tokens < 1 || !seg->pos_id) return fail(MIS_ERR_ARG, "seg is not a built segment descriptor");
-  mis::RopeFreq f{};
-  for (int i = 0; i < head_dim / 2; ++i) f.inv[i] = std::pow(double(theta), -2.0 * i / head_dim);
-  hipError_t e = mis::launch_rope(*seg, q, k, dt, hq, hkv, head_dim, f, static_cast<hipStream_t>(stream));
+  const mis::RopeFreq f = rope_freq(theta, head_dim);
+  hipError_t e =
+      mis::launch_rope(*seg, q, k, dt, q ? hq : 0, hkv, head_dim, f, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rope launch");
+  return ok();
+}
+
+int mis_rope_table_bytes(int32_t num_positions, int32_t head_dim, size_t *bytes) {
+  if (!bytes) return fail(MIS_ERR_ARG, "bytes is NULL");
+  if (num_positions < 1) return fail(MIS_ERR_ARG, "num_positions must be >= 1 (got %d)", num_positions);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(MIS_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  *bytes = size_t(num_positions) * size_t(head_dim) * sizeof(float);
+  return ok();
+}
+
+int mis_rope_table(int32_t num_positions, int32_t head_dim, float theta, void *table, size_t table_bytes,
+                   void *stream) {
+  size_t need = 0;
+  int rc = mis_rope_table_bytes(num_positions, head_dim, &need);
+  if (rc) return rc;
+  if (!table) return fail(MIS_ERR_ARG, "table is NULL");
+  if (table_bytes < need) return fail(MIS_ERR_ARG, "table of %zu bytes, need %zu", table_bytes, need);
+  if (!(theta > 0.f) || !std::isfinite(theta)) return fail(MIS_ERR_ARG, "theta must be a positive finite number");
+  const mis::RopeFreq f = rope_freq(theta, head_dim);
+  hipError_t e = mis::launch_rope_table(static_cast<float *>(table), num_positions, head_dim, f,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
   return ok();
 }
 

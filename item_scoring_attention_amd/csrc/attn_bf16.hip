@@ -63,6 +63,7 @@
 
 #include "gfx950_util.h"
 #include "mis_internal.h"
+#include "rope_math.h"
 
 namespace mis {
 namespace {
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(64 * TB * HP, HP == 2 ? 2 : 1) void attn_dma_kernel
     const int32_t *__restrict__ prefix_lens, const int32_t *__restrict__ cu_tiles,
     const int8_t *__restrict__ tile_class, const int32_t *__restrict__ pos_id, const __bf16 *__restrict__ q,
     const __bf16 *__restrict__ k, const __bf16 *__restrict__ v, __bf16 *__restrict__ o, int hq,
-    int hkv, float c /* softmax scale * log2(e) */, int items_only) {
+    int hkv, float c /* softmax scale * log2(e) */, int items_only, const float *__restrict__ rope_cs) {
   constexpr int NW = TB * HP;             // waves
   constexpr int BMT = 32 * TB;            // query tokens per workgroup
   constexpr int TILE = BN * D;            // bf16 elements of one K or V tile
@@ -307,6 +308,22 @@ __global__ __launch_bounds__(64 * TB * HP, HP == 2 ? 2 : 1) void attn_dma_kernel
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       qf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qo + 32u * kk, 0, 0));
+  }
+  // Q rotated here when the caller passes the rotary table (cos, sin of every
+  // position and pair): qf[kk] and qf[kk + 4] hold the two halves of the
+  // lane's pairs 16 kk + 8 g .. + 7. Rows past the request end are zeros.
+  if (rope_cs) {
+    const float4 *tp = reinterpret_cast<const float4 *>(rope_cs + int64_t(row_ok ? pos_id[base + j] : 0) * D);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      float cs[16];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 t = tp[8 * kk + 4 * g + u];
+        cs[4 * u] = t.x, cs[4 * u + 1] = t.y, cs[4 * u + 2] = t.z, cs[4 * u + 3] = t.w;
+      }
+      rope_rotate8(qf[kk], qf[kk + 4], cs);
+    }
   }
 
   // DMA lane mapping: instruction i of this wave covers tile rows
@@ -425,12 +442,12 @@ int device_cus() {
 
 template <int TB, int HP>
 hipError_t launch_variant(const mis_segments &seg, const __bf16 *qp, const __bf16 *kp, const __bf16 *vp,
-                          __bf16 *op, int hq, int hkv, float c, int items_only, hipStream_t st) {
+                          __bf16 *op, int hq, int hkv, float c, int items_only, const float *rope_cs, hipStream_t st) {
   const int64_t blocks = int64_t(seg.num_work) * hq / HP;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   attn_dma_kernel<TB, HP><<<dim3(unsigned(blocks)), 64 * TB * HP, 0, st>>>(
       seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.pos_id, qp, kp, vp, op,
-      hq, hkv, c, items_only);
+      hq, hkv, c, items_only, rope_cs);
   return hipGetLastError();
 }
 
@@ -478,7 +495,7 @@ const char *attention_bf16_name(AttnKernel k) {
 
 hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const void *k,
                                  const void *v, void *o, int hq, int hkv, int d, float scale,
-                                 int items_only, AttnKernel kernel, hipStream_t st) {
+                                 int items_only, AttnKernel kernel, const float *rope_cs, hipStream_t st) {
   if (d != D) return hipErrorInvalidValue;
   const float c = scale * kLog2e;
   const __bf16 *qp = static_cast<const __bf16 *>(q);
@@ -486,11 +503,14 @@ hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const v
   const __bf16 *vp = static_cast<const __bf16 *>(v);
   __bf16 *op = static_cast<__bf16 *>(o);
   switch (kernel) {
-    case AttnKernel::Pipe4: return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, 4, st);
-    case AttnKernel::Pipe2: return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, 2, st);
-    case AttnKernel::Pipe32: return launch_attention_bf16_pipe32(seg, q, k, v, o, hq, hkv, scale, items_only, st);
-    case AttnKernel::Classic2: return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
-    case AttnKernel::Classic1: return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, items_only, st);
+    case AttnKernel::Pipe4:
+      return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, 4, rope_cs, st);
+    case AttnKernel::Pipe2:
+      return launch_attention_bf16_pipe(seg, q, k, v, o, hq, hkv, scale, items_only, 2, rope_cs, st);
+    case AttnKernel::Pipe32:
+      return launch_attention_bf16_pipe32(seg, q, k, v, o, hq, hkv, scale, items_only, rope_cs, st);
+    case AttnKernel::Classic2: return launch_variant<2, 2>(seg, qp, kp, vp, op, hq, hkv, c, items_only, rope_cs, st);
+    case AttnKernel::Classic1: return launch_variant<2, 1>(seg, qp, kp, vp, op, hq, hkv, c, items_only, rope_cs, st);
   }
   return hipErrorInvalidValue;
 }

@@ -45,11 +45,13 @@
 #include "attn_loop.inc"
 #include "gfx950_util.h"
 #include "mis_internal.h"
+#include "rope_math.h"
 
 namespace mis {
 namespace {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x32 __attribute__((ext_vector_type(32)));
 
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
     const int32_t *__restrict__ prefix_lens, const int32_t *__restrict__ cu_tiles,
     const int8_t *__restrict__ tile_class, const int32_t *__restrict__ pos_id, const __bf16 *__restrict__ q,
     const __bf16 *__restrict__ k, const __bf16 *__restrict__ v, __bf16 *__restrict__ o, int hq,
-    int hkv, float c, int items_only) {
+    int hkv, float c, int items_only, const float *__restrict__ rope_cs) {
   constexpr int NW = HP * TB;                // waves
   constexpr int QB = 2 / TB;                 // 32-row query blocks per wave
   constexpr int ROWS_PER_WAVE = BN / NW;     // tile rows each wave loads
@@ -343,6 +345,35 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
     x.rjb[qb] = jb - 4 * g;
   }
 
+  // Q rotated here when the caller passes the rotary table (cos, sin of
+  // every position and pair, the rotation pass's values): lane half g holds
+  // dims 16 kk + 8 g .. + 7 of both halves of its head row (kk and kk + 4),
+  // so every pair (i, i + 64) is in the lane's own registers.
+  if (rope_cs) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float4 *tp = reinterpret_cast<const float4 *>(rope_cs + int64_t(pos[qb]) * D);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        float cs[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float4 t = tp[8 * kk + 4 * g + u];
+          cs[4 * u] = t.x, cs[4 * u + 1] = t.y, cs[4 * u + 2] = t.z, cs[4 * u + 3] = t.w;
+        }
+        f32x4 flo, fhi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) flo[e] = qv[qb][4 * kk + e], fhi[e] = qv[qb][4 * (kk + 4) + e];
+        bf16x8 lo = __builtin_bit_cast(bf16x8, flo), hi = __builtin_bit_cast(bf16x8, fhi);
+        rope_rotate8(lo, hi, cs);
+        flo = __builtin_bit_cast(f32x4, lo);
+        fhi = __builtin_bit_cast(f32x4, hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[qb][4 * kk + e] = flo[e], qv[qb][4 * (kk + 4) + e] = fhi[e];
+      }
+    }
+  }
+
   f32x32 o0, o1, o2, o3;
   float l0, l1 = 1.f;
   if constexpr (QB == 2)
@@ -378,35 +409,37 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
 
 template <int HP, int TB>
 hipError_t launch_pipe(const mis_segments &seg, const void *q, const void *k, const void *v, void *o, int hq,
-                       int hkv, float c, int items_only, hipStream_t st) {
+                       int hkv, float c, int items_only, const float *rope_cs, hipStream_t st) {
   const int64_t blocks = int64_t(seg.num_work) * hq / HP;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   attn_pipe_kernel<HP, TB><<<dim3(unsigned(blocks)), 64 * HP * TB, 0, st>>>(
       seg.work, seg.cu_seqlens, seg.prefix_lens, seg.cu_tiles, seg.tile_class, seg.pos_id,
       static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k), static_cast<const __bf16 *>(v),
-      static_cast<__bf16 *>(o), hq, hkv, c, items_only);
+      static_cast<__bf16 *>(o), hq, hkv, c, items_only, rope_cs);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention_bf16_pipe(const mis_segments &seg, const void *q, const void *k, const void *v, void *o,
-                                      int hq, int hkv, float scale, int items_only, int heads, hipStream_t st) {
+                                      int hq, int hkv, float scale, int items_only, int heads, const float *rope_cs,
+                                      hipStream_t st) {
   const int gsz = hq / hkv;
   if (gsz % heads != 0 || (heads != 2 && heads != 4)) return hipErrorInvalidValue;
   const float c = scale * kLog2e;
   // 4 heads per workgroup share each staged K/V tile among 4 waves (one
   // workgroup per CU, a 4-stage ring); 2 heads run two workgroups per CU.
-  if (heads == 4) return launch_pipe<4, 1>(seg, q, k, v, o, hq, hkv, c, items_only, st);
-  return launch_pipe<2, 1>(seg, q, k, v, o, hq, hkv, c, items_only, st);
+  if (heads == 4) return launch_pipe<4, 1>(seg, q, k, v, o, hq, hkv, c, items_only, rope_cs, st);
+  return launch_pipe<2, 1>(seg, q, k, v, o, hq, hkv, c, items_only, rope_cs, st);
 }
 
 hipError_t launch_attention_bf16_pipe32(const mis_segments &seg, const void *q, const void *k, const void *v,
-                                        void *o, int hq, int hkv, float scale, int items_only, hipStream_t st) {
+                                        void *o, int hq, int hkv, float scale, int items_only, const float *rope_cs,
+                                        hipStream_t st) {
   const int gsz = hq / hkv;
   if (gsz % 2 != 0) return hipErrorInvalidValue;
   // 2 heads x 2 row blocks of 32 per workgroup, two workgroups per CU.
-  return launch_pipe<2, 2>(seg, q, k, v, o, hq, hkv, scale * kLog2e, items_only, st);
+  return launch_pipe<2, 2>(seg, q, k, v, o, hq, hkv, scale * kLog2e, items_only, rope_cs, st);
 }
 
 }  // namespace mis

@@ -64,30 +64,36 @@ enum class AttnForce : int { Auto = 0, Pipe = 1, Pipe32 = 2, Classic = 3, Pipe2 
 AttnKernel pick_attention_bf16(const mis_segments &seg, int hq, int hkv, AttnForce force);
 const char *attention_bf16_name(AttnKernel k);
 
+// rope_cs: NULL, or the rotary table [positions][d/2] of float (cos, sin)
+// pairs; Q is then rotated at the rows' position ids as it is loaded.
 hipError_t launch_attention_bf16(const mis_segments &seg, const void *q, const void *k,
                                  const void *v, void *o, int hq, int hkv, int d, float scale,
-                                 int items_only, AttnKernel kernel, hipStream_t stream);
+                                 int items_only, AttnKernel kernel, const float *rope_cs, hipStream_t stream);
 
 // 64 query rows per wave, software-pipelined key-tile loop, `heads` (2 or 4,
 // dividing the GQA group) query heads per workgroup, head_dim 128;
 // launch_attention_bf16 dispatches to it.
 hipError_t launch_attention_bf16_pipe(const mis_segments &seg, const void *q, const void *k,
                                       const void *v, void *o, int hq, int hkv, float scale,
-                                      int items_only, int heads, hipStream_t stream);
+                                      int items_only, int heads, const float *rope_cs, hipStream_t stream);
 
 // The same loop with 32 query rows per wave, two waves per SIMD (even GQA
 // group sizes, head_dim 128).
 hipError_t launch_attention_bf16_pipe32(const mis_segments &seg, const void *q, const void *k,
                                         const void *v, void *o, int hq, int hkv, float scale,
-                                        int items_only, hipStream_t stream);
+                                        int items_only, const float *rope_cs, hipStream_t stream);
 
 // Inverse frequencies theta^(-2i/D) of the rotary embedding, i < D/2.
 struct RopeFreq {
   double inv[64];
 };
 
+// Rotates Q (hq heads; q may be NULL with hq == 0) and K in place at the
+// segment position ids.
 hipError_t launch_rope(const mis_segments &seg, void *q, void *k, mis_dtype dt, int hq, int hkv, int d,
                        const RopeFreq &freq, hipStream_t stream);
+// table [npos][d/2] of float (cos, sin) pairs, the rotation pass's angles.
+hipError_t launch_rope_table(float *table, int npos, int d, const RopeFreq &freq, hipStream_t stream);
 
 // Scoring workspace layout: partial maxima [nvt][N], partial sum-exp
 // [nvt][N], label logits [N][K] (all float32), then N int32 readout

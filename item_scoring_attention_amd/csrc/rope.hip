@@ -7,17 +7,20 @@
 // pos * theta^(-2i/D).
 //
 // One thread owns 8 consecutive pairs of one token in up to 4 of its head rows
-// (query heads first, then KV heads): it computes the 8 angles (product and
-// reduction modulo 2*pi in fp64, then sin/cos in fp32), issues all its loads,
-// then rotates and stores. A head row is a 2*D-byte contiguous run read by
-// D/16 threads. HBM-bound: every Q and K byte is read and written once.
+// (query heads first, then KV heads; KV heads only when Q is rotated inside
+// the attention call): it computes the 8 angles (product and reduction modulo
+// 2*pi in fp64, then sin/cos in fp32), issues all its loads, then rotates and
+// stores. A head row is a 2*D-byte contiguous run read by D/16 threads.
+// HBM-bound: every rotated byte is read and written once.
+//
+// The cos/sin table (rope_table_kernel) holds the same angles for positions
+// 0 .. P-1, for the attention kernels that rotate Q while loading it.
 #include "mis_internal.h"
+#include "rope_math.h"
 
 namespace mis {
 namespace {
 
-constexpr double kTwoPi = 6.283185307179586476925286766559;
-constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 constexpr int kPairsPerThread = 8;
 
 template <typename T>
@@ -69,11 +72,7 @@ __global__ __launch_bounds__(256) void rope_kernel(const int32_t *__restrict__ p
   const double pos = double(pos_id[t]);
   float cs[kPairsPerThread], sn[kPairsPerThread];
 #pragma unroll
-  for (int e = 0; e < kPairsPerThread; ++e) {
-    double a = pos * freq.inv[i0 + e];
-    a -= kTwoPi * rint(a * kInvTwoPi);
-    sincosf(float(a), &sn[e], &cs[e]);
-  }
+  for (int e = 0; e < kPairsPerThread; ++e) rope_cos_sin(pos, freq.inv[i0 + e], cs[e], sn[e]);
   T *rows[kHeadsPerThread];
   float a[kHeadsPerThread][8], b[kHeadsPerThread][8];
 #pragma unroll
@@ -86,15 +85,22 @@ __global__ __launch_bounds__(256) void rope_kernel(const int32_t *__restrict__ p
 #pragma unroll
   for (int u = 0; u < kHeadsPerThread; ++u) {
     if (hb * kHeadsPerThread + u >= heads) break;
-    float ra[8], rb[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ra[e] = a[u][e] * cs[e] - b[u][e] * sn[e];
-      rb[e] = b[u][e] * cs[e] + a[u][e] * sn[e];
-    }
-    Vec8<T>::store(rows[u] + i0, ra);
-    Vec8<T>::store(rows[u] + HALF + i0, rb);
+    for (int e = 0; e < 8; ++e) rope_rotate(a[u][e], b[u][e], cs[e], sn[e]);
+    Vec8<T>::store(rows[u] + i0, a[u]);
+    Vec8<T>::store(rows[u] + HALF + i0, b[u]);
   }
+}
+
+// table[p][i] = (cos, sin) of the angle of pair i at position p, p < npos.
+template <int D>
+__global__ __launch_bounds__(256) void rope_table_kernel(float2 *__restrict__ table, int npos, RopeFreq freq) {
+  constexpr int HALF = D / 2;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= int64_t(npos) * HALF) return;
+  float c, s;
+  rope_cos_sin(double(idx / HALF), freq.inv[idx % HALF], c, s);
+  table[idx] = make_float2(c, s);
 }
 
 template <typename T, int D>
@@ -108,6 +114,16 @@ hipError_t launch(const mis_segments &seg, T *q, T *k, int hq, int hkv, const Ro
 }
 
 }  // namespace
+
+hipError_t launch_rope_table(float *table, int npos, int d, const RopeFreq &f, hipStream_t st) {
+  const int64_t blocks = (int64_t(npos) * (d / 2) + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (blocks == 0) return hipSuccess;
+  float2 *t = reinterpret_cast<float2 *>(table);
+  if (d == 128) rope_table_kernel<128><<<unsigned(blocks), 256, 0, st>>>(t, npos, f);
+  else rope_table_kernel<64><<<unsigned(blocks), 256, 0, st>>>(t, npos, f);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope(const mis_segments &seg, void *q, void *k, mis_dtype dt, int hq, int hkv, int d,
                        const RopeFreq &f, hipStream_t st) {

@@ -336,6 +336,75 @@ __global__ __launch_bounds__(256) void score_lds_kernel(
   }
 }
 
+// Epilogue of the 256-row tiles: element a of acc[mi][ni] of wave w, lane
+// (g, ql) is z[row v0 + 64w + 32mi + 8(a/4) + 4g + a%4][item n0 + 32ni + ql].
+// Per item: (max, sum exp) over the tile's rows below V, through the 4-wave
+// exchange red; label logits copied out exactly by the lane that holds them.
+template <int NI>
+__device__ __forceinline__ void wide_epilogue(const f32x16 (&acc)[2][NI], float (&red)[4][NI][32], int v0, int vt,
+                                              int n0, int V, int N, const LabelArgs &labels, float *pmax,
+                                              float *psum, float *plab) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 5, ql = lane & 31;
+  auto row_of = [&](int mi, int a) { return v0 + 64 * wave + 32 * mi + 8 * (a >> 2) + 4 * g + (a & 3); };
+  float m[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    float x = -INFINITY;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int a = 0; a < 16; ++a)
+        if (row_of(mi, a) < V) x = fmaxf(x, acc[mi][ni][a]);
+    x = fmaxf(x, __shfl_xor(x, 32));
+    if (g == 0) red[wave][ni][ql] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    m[ni] = fmaxf(fmaxf(red[0][ni][ql], red[1][ni][ql]), fmaxf(red[2][ni][ql], red[3][ni][ql]));
+  __syncthreads();
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    float sum = 0.f;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int a = 0; a < 16; ++a)
+        if (row_of(mi, a) < V) sum += fast_exp(acc[mi][ni][a] - m[ni]);
+    sum += __shfl_xor(sum, 32);
+    if (g == 0) red[wave][ni][ql] = sum;
+  }
+  __syncthreads();
+  if (wave == 0 && g == 0) {
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int n = n0 + 32 * ni + ql;
+      if (n < N) {
+        pmax[int64_t(vt) * N + n] = m[ni];
+        psum[int64_t(vt) * N + n] = red[0][ni][ql] + red[1][ni][ql] + red[2][ni][ql] + red[3][ni][ql];
+      }
+    }
+  }
+  for (int kx = 0; kx < labels.k; ++kx) {
+    const int ro = labels.ids[kx] - v0 - 64 * wave;
+    if (ro < 0 || ro >= 64) continue;
+    const int mi = ro >> 5, rr = ro & 31;
+    if (((rr >> 2) & 1) != g) continue;
+    const int at = 4 * (rr >> 3) + (rr & 3);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      float z = 0.f;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) z = (a == at) ? (mi ? acc[1][ni][a] : acc[0][ni][a]) : z;
+      const int n = n0 + 32 * ni + ql;
+      if (n < N) plab[int64_t(n) * labels.k + kx] = z;
+    }
+  }
+}
+
 // ------------------------------- bf16 LDS-staged, wide tiles (H % 64 == 0)
 // For many items the contraction is MFMA-bound, and with 32 vocabulary rows
 // per wave the fragment reads (one W fragment and NI readout fragments per
@@ -469,63 +538,7 @@ __global__ __launch_bounds__(256, 1) void score_wide_kernel(
     slot = slot + 1 == NS ? 0 : slot + 1;
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing loads land before the workgroup ends
-
-  // element a of acc[mi][ni] is z[row v0 + 64*wave + 32*mi + 8*(a/4) + 4*g + a%4][item n0 + 32*ni + ql]
-  auto row_of = [&](int mi, int a) { return v0 + 64 * wave + 32 * mi + 8 * (a >> 2) + 4 * g + (a & 3); };
-  float m[NI];
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    float x = -INFINITY;
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int a = 0; a < 16; ++a)
-        if (row_of(mi, a) < V) x = fmaxf(x, acc[mi][ni][a]);
-    x = fmaxf(x, __shfl_xor(x, 32));
-    if (g == 0) red[wave][ni][ql] = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni)
-    m[ni] = fmaxf(fmaxf(red[0][ni][ql], red[1][ni][ql]), fmaxf(red[2][ni][ql], red[3][ni][ql]));
-  __syncthreads();
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) {
-    float sum = 0.f;
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int a = 0; a < 16; ++a)
-        if (row_of(mi, a) < V) sum += fast_exp(acc[mi][ni][a] - m[ni]);
-    sum += __shfl_xor(sum, 32);
-    if (g == 0) red[wave][ni][ql] = sum;
-  }
-  __syncthreads();
-  if (wave == 0 && g == 0) {
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const int n = n0 + 32 * ni + ql;
-      if (n < N) {
-        pmax[int64_t(vt) * N + n] = m[ni];
-        psum[int64_t(vt) * N + n] = red[0][ni][ql] + red[1][ni][ql] + red[2][ni][ql] + red[3][ni][ql];
-      }
-    }
-  }
-  for (int kx = 0; kx < labels.k; ++kx) {
-    const int ro = labels.ids[kx] - v0 - 64 * wave;
-    if (ro < 0 || ro >= 64) continue;
-    const int mi = ro >> 5, rr = ro & 31;
-    if (((rr >> 2) & 1) != g) continue;
-    const int at = 4 * (rr >> 3) + (rr & 3);
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      float z = 0.f;
-#pragma unroll
-      for (int a = 0; a < 16; ++a) z = (a == at) ? (mi ? acc[1][ni][a] : acc[0][ni][a]) : z;
-      const int n = n0 + 32 * ni + ql;
-      if (n < N) plab[int64_t(n) * labels.k + kx] = z;
-    }
-  }
+  wide_epilogue<NI>(acc, red, v0, vt, n0, V, N, labels, pmax, psum, plab);
 }
 
 // ---------------------------------------------------------------- fp32

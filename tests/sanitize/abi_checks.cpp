@@ -22,6 +22,13 @@ bool expect(const char *what, int got, int want) {
   return false;
 }
 
+bool expect_true(const char *what, bool cond) {
+  ++g_checks;
+  if (cond) return true;
+  std::fprintf(stderr, "FAILED %s\n", what);
+  return false;
+}
+
 // A fake device address: the checks below fail before it could be used.
 void *const kFakeDev = reinterpret_cast<void *>(uintptr_t(0x100000));
 
@@ -122,6 +129,23 @@ int main() {
   ok &= expect("rope theta 0", mis_apply_rope(&s, t, t, MIS_BF16, 16, 8, 128, 0.f, nullptr), MIS_ERR_ARG);
   ok &= expect("rope theta inf", mis_apply_rope(&s, t, t, MIS_BF16, 16, 8, 128, INFINITY, nullptr), MIS_ERR_ARG);
   ok &= expect("rope head_dim 96", mis_apply_rope(&s, t, t, MIS_BF16, 16, 8, 96, 1e4f, nullptr), MIS_ERR_UNSUPPORTED);
+  ok &= expect("rope NULL k", mis_apply_rope(&s, t, nullptr, MIS_BF16, 16, 8, 128, 1e4f, nullptr), MIS_ERR_ARG);
+  ok &= expect("rope K only, no device", mis_apply_rope(&s, nullptr, t, MIS_BF16, 16, 8, 128, 1e4f, nullptr),
+               MIS_ERR_HIP);
+  ok &= expect("rope table bytes", mis_rope_table_bytes(100, 128, &bytes), MIS_OK);
+  ok &= expect_true("rope table bytes value", bytes == size_t(100) * 128 * 4);
+  ok &= expect("rope table 0 positions", mis_rope_table_bytes(0, 128, &bytes), MIS_ERR_ARG);
+  ok &= expect("rope table short buffer", mis_rope_table(100, 128, 1e4f, t, 100 * 128 * 4 - 1, nullptr), MIS_ERR_ARG);
+  ok &= expect("rope table, no device", mis_rope_table(100, 128, 1e4f, t, 100 * 128 * 4, nullptr), MIS_ERR_HIP);
+  ok &= expect("fused rope NULL table",
+               mis_attention_prefill_rope(&s, t, t, t, t, MIS_BF16, 16, 8, 128, 0.f, nullptr, 1000, nullptr),
+               MIS_ERR_ARG);
+  ok &= expect("fused rope short table",
+               mis_attention_prefill_rope(&s, t, t, t, t, MIS_BF16, 16, 8, 128, 0.f, t, s.max_seqlen - 1, nullptr),
+               MIS_ERR_ARG);
+  ok &= expect("fused rope valid, no device",
+               mis_attention_append_rope(&s, t, t, t, t, MIS_BF16, 16, 8, 128, 0.f, t, s.max_seqlen, nullptr),
+               MIS_ERR_HIP);
 
   // ---- scoring
   const int32_t labels[] = {3, 7}, bad_label[] = {3, 1000};

@@ -18,13 +18,14 @@ hipError_t launch_attention_f32(const mis_segments &, const float *, const float
 AttnKernel pick_attention_bf16(const mis_segments &, int, int, AttnForce) { return AttnKernel::Pipe32; }
 const char *attention_bf16_name(AttnKernel) { return "stub"; }
 hipError_t launch_attention_bf16(const mis_segments &, const void *, const void *, const void *, void *, int, int, int,
-                                 float, int, AttnKernel, hipStream_t) {
+                                 float, int, AttnKernel, const float *, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t launch_rope(const mis_segments &, void *, void *, mis_dtype, int, int, int, const RopeFreq &,
                        hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t launch_rope_table(float *, int, int, const RopeFreq &, hipStream_t) { return hipErrorNoDevice; }
 ScoreKernel pick_score(int, int, mis_dtype, ScoreForce, int) { return {ScoreKind::Narrow, 1}; }
 void score_kernel_name(const ScoreKernel &, char *buf, size_t n) {
   if (n) buf[0] = 0;

@@ -208,7 +208,11 @@ def test_rope_argument_errors():
     p = ctypes.c_void_p(0x1000)
     call = lambda seg, q, dt, hq, hkv, d, theta=1e4: lib.mis_apply_rope(seg, q, p, dt, hq, hkv, d, theta, None)
     assert call(None, p, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_ARG
+    assert lib.mis_apply_rope(ctypes.byref(s), p, None, mis.MIS_BF16, 8, 4, 128, 1e4, None) == mis.MIS_ERR_ARG
+    assert "k must be" in mis.last_error()
+    # q may be NULL (K rotated alone): the checks then stop at the missing position ids
     assert call(ctypes.byref(s), None, mis.MIS_BF16, 8, 4, 128) == mis.MIS_ERR_ARG
+    assert "not a built segment" in mis.last_error()
     assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 3, 128) == mis.MIS_ERR_ARG
     assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 4, 80) == mis.MIS_ERR_UNSUPPORTED
     assert call(ctypes.byref(s), p, 7, 8, 4, 128) == mis.MIS_ERR_UNSUPPORTED
@@ -216,6 +220,37 @@ def test_rope_argument_errors():
         assert call(ctypes.byref(s), p, mis.MIS_BF16, 8, 4, 128, theta) == mis.MIS_ERR_ARG
     assert call(ctypes.byref(s), p, mis.MIS_F32, 8, 4, 64) == mis.MIS_ERR_ARG  # no position ids
     assert "not a built segment" in mis.last_error()
+
+
+def test_rope_table_and_fused_attention_argument_errors():
+    lib = mis.load()
+    out = ctypes.c_size_t(0)
+    assert lib.mis_rope_table_bytes(100, 128, ctypes.byref(out)) == mis.MIS_OK and out.value == 100 * 128 * 4
+    assert lib.mis_rope_table_bytes(7, 64, ctypes.byref(out)) == mis.MIS_OK and out.value == 7 * 64 * 4
+    assert lib.mis_rope_table_bytes(0, 128, ctypes.byref(out)) == mis.MIS_ERR_ARG
+    assert lib.mis_rope_table_bytes(10, 96, ctypes.byref(out)) == mis.MIS_ERR_UNSUPPORTED
+    assert lib.mis_rope_table_bytes(10, 128, None) == mis.MIS_ERR_ARG
+    assert mis.mis_rope_table_bytes(33, 128) == 33 * 128 * 4
+    p = ctypes.c_void_p(0x1000)
+    # rejected before anything is enqueued
+    assert lib.mis_rope_table(10, 128, 1e4, None, 5120, None) == mis.MIS_ERR_ARG
+    assert lib.mis_rope_table(10, 128, 1e4, p, 5119, None) == mis.MIS_ERR_ARG
+    for theta in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.mis_rope_table(10, 128, theta, p, 5120, None) == mis.MIS_ERR_ARG
+    s = _fake_seg()
+    s.max_seqlen = 100
+    for fn in (lib.mis_attention_prefill_rope, lib.mis_attention_append_rope):
+        call = lambda dt, table, npos, d=128, seg=s: fn(ctypes.byref(seg), p, p, p, p, dt, 8, 4, d, 0.0, table,
+                                                        npos, None)
+        assert call(mis.MIS_BF16, None, 100) == mis.MIS_ERR_ARG
+        assert "rope_table" in mis.last_error()
+        assert call(mis.MIS_BF16, p, 99) == mis.MIS_ERR_ARG
+        assert "short" in mis.last_error()
+        bm, bn = mis.mis_attention_tile_shape(mis.MIS_F32, 8, 4, 64)
+        s32 = _fake_seg(bm=bm, bn=bn)
+        s32.max_seqlen = 100
+        assert call(mis.MIS_F32, p, 100, d=64, seg=s32) == mis.MIS_ERR_UNSUPPORTED
+        assert "bf16 only" in mis.last_error()
 
 
 def test_score_at_argument_errors():

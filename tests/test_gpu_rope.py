@@ -93,3 +93,118 @@ def test_mis_with_rope_equals_single_item_scoring(dtype, d, tol):
     torch.cuda.synchronize()
     sis = oracle.sis_rope_attention(q, k, v, wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, 1e4)
     assert np.abs(oracle.as_f64(o) - sis).max() <= tol
+
+
+# ------------------------------------------------ Q rotated inside attention
+
+KERNELS = ["auto", "pipe", "pipe2", "pipe32", "classic"]
+
+
+def _fits(choice, wl):
+    gsz = wl.hq // wl.hkv
+    if choice == "pipe":
+        return gsz % 4 == 0
+    if choice in ("pipe2", "pipe32"):
+        return gsz % 2 == 0
+    return True
+
+
+def test_rope_table_values():
+    """cos and sin of p * theta^(-2i/D) for every position and pair: the
+    oracle's rotation of the unit vector (1, 0) at position p gives them."""
+    for d, theta in ((128, 1e6), (64, 1e4)):
+        P = 3000
+        t = mis.mis_rope_table(P, d, theta)
+        torch.cuda.synchronize()
+        got = host(t).astype(np.float64).reshape(P, d // 2, 2)
+        unit = np.zeros((P, 1, d), dtype=np.float32)
+        unit[:, 0, : d // 2] = 1.0
+        rot = oracle.rope(unit, np.arange(P), theta)[:, 0, :]  # (cos, sin) of each pair's angle
+        assert np.abs(got[:, :, 0] - rot[:, : d // 2]).max() <= 1e-6
+        assert np.abs(got[:, :, 1] - rot[:, d // 2:]).max() <= 1e-6
+
+
+def _fused_vs_separate(wl, choice, theta=1e6, append=False):
+    """Fused: K rotated alone, Q rotated by the attention kernel. Separate:
+    both rotated by the rotation pass, then the plain attention call. The
+    outputs must agree bit for bit, and the caller's Q stay untouched."""
+    q, k, v = workloads.qkv(wl)
+    seg = build(wl)
+    table = mis.mis_rope_table(seg.max_seqlen, wl.d, theta)
+    mis.set_kernel_choice(attention=choice)
+    try:
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        mis.mis_apply_rope(seg, None, kd, theta)
+        o_f = nan_like(qd)
+        if append:
+            mis.mis_attention_append_rope(seg, qd, kd, vd, o_f, table)
+        else:
+            mis.mis_attention_prefill_rope(seg, qd, kd, vd, table, o=o_f)
+        q2, k2 = dev(q), dev(k)
+        mis.mis_apply_rope(seg, q2, k2, theta)
+        o_s = nan_like(qd)
+        if append:
+            mis.mis_attention_append(seg, q2, k2, vd, o_s)
+        else:
+            mis.mis_attention_prefill(seg, q2, k2, vd, o=o_s)
+        torch.cuda.synchronize()
+    finally:
+        mis.set_kernel_choice()
+    assert np.array_equal(host(qd), q), "q was modified"
+    assert np.array_equal(host(kd), host(k2)), "K rotated alone differs from K rotated with Q"
+    of, os_ = host(o_f), host(o_s)
+    if append:
+        items = segments_oracle(wl)["item_id"] >= 0
+        of, os_ = of[items], os_[items]
+    assert np.array_equal(of, os_), f"{choice}: fused and separate rotation differ"
+    assert np.isfinite(oracle.as_f64(of)).all()
+    return q, k, v, of
+
+
+@pytest.mark.parametrize("choice", KERNELS)
+def test_fused_rope_small_shapes(choice):
+    for wl in (workloads.from_lengths("frope-gqa4", [70, 5, 130], [[4, 1, 33, 8], [2, 17], [20] * 5],
+                                      hq=16, hkv=4, d=128, seed=31),
+               workloads.from_lengths("frope-gqa2", [200, 0], [[3, 65, 9], [4, 4]], hq=8, hkv=4, d=128, seed=32),
+               workloads.from_lengths("frope-mha", [33], [[7, 7, 40]], hq=4, hkv=4, d=128, seed=33)):
+        if not _fits(choice, wl):
+            continue
+        say(f"[fused rope] {wl.name} {choice}")
+        q, k, v, o = _fused_vs_separate(wl, choice)
+        sis = oracle.sis_rope_attention(q, k, v, wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts, 1e6)
+        assert np.abs(oracle.as_f64(o) - sis).max() <= TOL_BF16_ATTN
+
+
+@pytest.mark.parametrize("choice", KERNELS)
+def test_fused_rope_single_request_workload(choice):
+    wl = workloads.config(2)
+    say(f"[fused rope] {wl.name} {choice}")
+    _fused_vs_separate(wl, choice)
+
+
+@pytest.mark.parametrize("choice", ["auto", "pipe32"])
+def test_fused_rope_append(choice):
+    wl = workloads.config(2)
+    say(f"[fused rope append] {wl.name} {choice}")
+    _fused_vs_separate(wl, choice, append=True)
+
+
+def test_fused_rope_long_prefix_workload():
+    wl = workloads.config(5)
+    say(f"[fused rope] {wl.name}")
+    _fused_vs_separate(wl, "auto")
+
+
+def test_fused_rope_rejects_short_table_and_f32():
+    wl = workloads.from_lengths("frope-err", [40], [[5, 6]], hq=8, hkv=4, d=128, seed=34)
+    q, k, v = workloads.qkv(wl)
+    seg = build(wl)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    short = mis.mis_rope_table(seg.max_seqlen - 1, 128, 1e4)
+    with pytest.raises(ValueError, match="short"):
+        mis.mis_attention_prefill_rope(seg, qd, kd, vd, short)
+    wl32 = workloads.from_lengths("frope-f32", [40], [[5, 6]], hq=8, hkv=4, d=64, dtype="f32", seed=35)
+    q32, k32, v32 = workloads.qkv(wl32)
+    seg32 = build(wl32)
+    with pytest.raises(mis.MisError):
+        mis.mis_attention_prefill_rope(seg32, dev(q32), dev(k32), dev(v32), mis.mis_rope_table(100, 64, 1e4))
