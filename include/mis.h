@@ -333,7 +333,10 @@ int mis_score_labels_at(const int32_t *positions_h, int32_t num_rows, int32_t nu
  *   score:     NULL, "" or "auto"; "narrow" (128 vocabulary rows x up to 128
  *              items per workgroup); "wide" (256 rows, item blocks by shape) or
  *              "wide3", "wide4", "wide5", "wide6", "wide8" (that many blocks of
- *              32 items). Applies to bf16 with hidden_size % 64 == 0.
+ *              32 items); "persist" or "persist3" .. "persist5" (the 256-row
+ *              tiles in persistent workgroups with loader waves; needs
+ *              hidden_size >= 128, else the wide tiles). Applies to bf16 with
+ *              hidden_size % 64 == 0.
  * Errors: ARG (unknown name; the previous setting stays).
  */
 int mis_set_kernel_choice(const char *attention, const char *score);
@@ -349,7 +352,7 @@ const char *mis_attention_kernel_name(const mis_segments *seg, mis_dtype dt, int
 /*
  * Name of the LM-head kernel that mis_score_labels launches on this thread
  * for num_items items of hidden size hidden_size, e.g.
- * "score_wide_kernel<8, 2>" (the combine kernel always follows it). Thread-
+ * "score_persist_kernel<5, 3>" (the combine kernel always follows it). Thread-
  * local storage, valid until the next call on this thread; never NULL.
  */
 const char *mis_score_kernel_name(int32_t num_items, int32_t hidden_size, mis_dtype dt);

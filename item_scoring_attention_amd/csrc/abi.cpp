@@ -655,8 +655,15 @@ int mis_set_kernel_choice(const char *attention, const char *score) {
   else if (!std::strncmp(score, "wide", 4) && score[4] >= '3' && score[4] <= '8' && score[4] != '7' && !score[5]) {
     sf = mis::ScoreForce::Wide;
     ni = score[4] - '0';
+  } else if (!std::strcmp(score, "persist")) {
+    sf = mis::ScoreForce::Persist;
+  } else if (!std::strncmp(score, "persist", 7) && score[7] >= '3' && score[7] <= '5' && !score[8]) {
+    sf = mis::ScoreForce::Persist;
+    ni = score[7] - '0';
   } else {
-    return fail(MIS_ERR_ARG, "unknown scoring kernel choice '%s' (auto, narrow, wide, wide3..wide6, wide8)", score);
+    return fail(MIS_ERR_ARG,
+                "unknown scoring kernel choice '%s' (auto, narrow, wide, wide3..wide6, wide8, persist, persist3..5)",
+                score);
   }
   g_attn_force = af;
   g_score_force = sf;

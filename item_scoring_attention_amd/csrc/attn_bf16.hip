@@ -427,19 +427,6 @@ __global__ __launch_bounds__(64 * TB * HP, HP == 2 ? 2 : 1) void attn_dma_kernel
   }
 }
 
-// Compute units of the current device (queried once per device).
-int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <int TB, int HP>
 hipError_t launch_variant(const mis_segments &seg, const __bf16 *qp, const __bf16 *kp, const __bf16 *vp,
                           __bf16 *op, int hq, int hkv, float c, int items_only, const float *rope_cs, hipStream_t st) {
@@ -452,6 +439,19 @@ hipError_t launch_variant(const mis_segments &seg, const __bf16 *qp, const __bf1
 }
 
 }  // namespace
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 AttnKernel pick_attention_bf16(const mis_segments &seg, int hq, int hkv, AttnForce force) {
   const int gsz = hq / hkv;

@@ -51,6 +51,9 @@ hipError_t launch_attention_f32(const mis_segments &seg, const float *q, const f
                                 const float *v, float *o, int hq, int hkv, int d, float scale,
                                 int items_only, hipStream_t stream);
 
+// Compute units of the current device (queried once per device).
+int device_cus();
+
 // The bf16 attention kernels and the rule that picks one per call.
 enum class AttnKernel : int {
   Pipe4 = 0,    // attn_pipe_kernel<4, 1>: 64 query rows per wave, 4 heads per workgroup
@@ -111,15 +114,18 @@ enum class ScoreKind : int {
   Wide = 1,    // score_wide_kernel<NI, NS>: 256 vocabulary rows x 32 NI items (NI 3, 4, 5, 6, 8)
   Global = 2,  // score_bf16_kernel<NI>: operands from global memory (H % 64 != 0)
   F32 = 3,     // score_f32_kernel
+  Persist = 4, // score_persist_kernel<NI, 3>: the wide tiles, persistent workgroups with loader waves
 };
 struct ScoreKernel {
   ScoreKind kind;
   int ni;  // item blocks of 32 per workgroup tile
 };
-// A caller's forced choice: Auto, the narrow tiles, or wide tiles with
-// force_ni item blocks (0: blocks chosen by shape). Ignored where the
-// forced kernel does not apply (fp32, H % 64 != 0).
-enum class ScoreForce : int { Auto = 0, Narrow = 1, Wide = 2 };
+// A caller's forced choice: Auto, the narrow tiles, wide tiles with
+// force_ni item blocks (0: blocks chosen by shape), or the persistent wide
+// tiles (item blocks 3-5). Ignored where the forced kernel does not apply
+// (fp32, H % 64 != 0; the persistent tiles need H >= 128 and fall back to
+// the wide ones).
+enum class ScoreForce : int { Auto = 0, Narrow = 1, Wide = 2, Persist = 3 };
 ScoreKernel pick_score(int num_rows, int h, mis_dtype dt, ScoreForce force, int force_ni);
 // Writes the kernel's name into buf (at most n bytes).
 void score_kernel_name(const ScoreKernel &k, char *buf, size_t n);

@@ -16,6 +16,7 @@
 // Pass 2 (one wave per item): merge the partials exactly,
 // lse = M + log(sum_c s_c * exp(m_c - M)), and write z_label - lse (or the
 // softmax over the label logits).
+#include <algorithm>
 #include <cstdio>
 #include <mutex>
 
@@ -541,6 +542,207 @@ __global__ __launch_bounds__(256, 1) void score_wide_kernel(
   wide_epilogue<NI>(acc, red, v0, vt, n0, V, N, labels, pmax, psum, plab);
 }
 
+// ---------------- bf16, wide tiles, persistent workgroups with loader waves
+// The 256-row x 32*NI-item tiles and LDS layout of score_wide_kernel, with
+// two changes. (1) Each workgroup loops over its share of the tiles (one
+// workgroup per CU), so the first chunks of its next tile are staged while
+// it finishes the current one: the per-tile start (readout positions, the
+// ring's first loads) leaves the critical path. (2) Waves 4-7 only stage
+// chunks into the LDS ring and waves 0-3 only read fragments and issue
+// MFMAs (one of each per SIMD), so no load instruction waits in front of an
+// MFMA. The loaders' vector-memory operations are all loads, so their counts
+// complete in order; the compute waves' epilogue stores never mix with them.
+template <int NI, int NS>
+__global__ __launch_bounds__(512, 1) void score_persist_kernel(
+    const __bf16 *__restrict__ hidden, const __bf16 *__restrict__ w, int H, int V, int N,
+    const int32_t *__restrict__ readout_pos, LabelArgs labels, float *__restrict__ pmax,
+    float *__restrict__ psum, float *__restrict__ plab, int nvt, int nit) {
+  constexpr int BVW = 256;                  // vocabulary rows of a tile
+  constexpr int NIT = 32 * NI;              // items of a tile
+  constexpr int WCH = BVW * 64;             // bf16 elements of a staged W chunk
+  constexpr int XCH = NIT * 64;             // ... and of a staged readout chunk
+  constexpr int PER_CHUNK = BVW / 32 + NI;  // loads per loader wave and chunk
+  struct Smem {
+    __bf16 w[NS][WCH];
+    __bf16 x[NS][XCH];
+    float red[4][NI][32];
+  };
+  static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) Smem sm;
+  auto &ws_ = sm.w;
+  auto &xs = sm.x;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cw = wave & 3;  // compute waves 0-3, loader waves 4-7 (one of each per SIMD)
+  const int lane = tid & 63;
+  const int g = lane >> 5, ql = lane & 31;
+  const int piece = lane & 7;
+  const int nch = H / 64;
+  // Tile k of this workgroup: jx = blockIdx / 8 + k * gridDim / 8 (gridDim is
+  // a multiple of 8, so all its tiles are on its XCD), vocabulary tile
+  // 8 (jx / nit) + XCD, item tile jx % nit: the item tiles of one vocabulary
+  // tile run on one XCD at about the same time and share its L2.
+  const int xcd = blockIdx.x & 7, j0 = blockIdx.x >> 3, J = gridDim.x >> 3;
+  const int vts = (nvt - xcd + 7) / 8;  // vocabulary tiles of this XCD
+  const int ntile = max(0, (vts * nit - j0 + J - 1) / J);
+  if (ntile == 0) return;
+  auto tile_vt = [&](int k) { return 8 * ((j0 + k * J) / nit) + xcd; };
+  auto tile_n0 = [&](int k) { return ((j0 + k * J) % nit) * NIT; };
+
+  if (wave >= 4) {
+    // ---- loader: chunk q of the workgroup's sequence (tile q / nch, chunk
+    // q % nch) goes to ring slot q % NS, NS - 1 chunks ahead of its use.
+    uint32_t woff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 64 * cw + 8 * i + (lane >> 3);
+      woff[i] = uint32_t(r) * uint32_t(H) * 2u + 16u * uint32_t(piece ^ ((r >> 1) & 7));
+    }
+    // first W row of a tile (V past the last tile: its loads read nothing)
+    auto w_row0 = [&](int k) { return __builtin_amdgcn_readfirstlane(k < ntile ? tile_vt(k) * BVW : V); };
+    // rows past V, and tiles past the last, read nothing (zero-length range);
+    // built from wave-uniform values where it is used, so it stays in scalar registers
+    auto w_rsrc = [&](int v0) {
+      const uint32_t rows = __builtin_amdgcn_readfirstlane(uint32_t(max(0, min(BVW, V - v0))));
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16 *>(w + int64_t(min(v0, V - 1)) * H), 0,
+                                               rows * uint32_t(H) * 2u, kRsrcWord3);
+    };
+    // readout positions of a tile's items (tiles past the last: item 0)
+    auto positions = [&](int k, int (&pos)[NI]) {
+      const int n0 = k < ntile ? tile_n0(k) : 0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) pos[i] = readout_pos[min(n0 + 32 * i + 8 * cw + (lane >> 3), N - 1)];
+    };
+    auto rows = [&](const int (&pos)[NI], const __bf16 *(&src)[NI]) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int n = 32 * i + 8 * cw + (lane >> 3);
+        src[i] = hidden + int64_t(pos[i]) * H + 8 * (piece ^ ((n >> 1) & 7));
+      }
+    };
+    int wv0 = w_row0(0), wv0_next = w_row0(1);
+    const __bf16 *xsrc[NI];
+    int pos_next[NI];
+    {
+      int pos0[NI];
+      positions(0, pos0);
+      rows(pos0, xsrc);
+      positions(1, pos_next);
+    }
+    auto issue = [&](int c, int slot) {
+      const __amdgpu_buffer_rsrc_t wrs = w_rsrc(wv0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        lds_load16(wrs, &ws_[slot][(64 * cw + 8 * i) * 64], woff[i] + 128u * uint32_t(c));
+#pragma unroll
+      for (int i = 0; i < NI; ++i) lds_load16(xsrc[i] + 64 * c, &xs[slot][(32 * i + 8 * cw) * 64]);
+    };
+    // the sequence's first NS - 1 chunks (all in tile 0: nch >= NS - 1)
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p) issue(p, p);
+    int ik = 0, ic = NS - 1, islot = NS - 1;  // next chunk to issue: tile ik, chunk ic, ring slot islot
+    for (int k = 0; k < ntile; ++k) {
+      for (int c = 0; c < nch; ++c) {
+        // chunk (k, c) landed: this wave's loads of it (NS - 2 chunks' loads,
+        // and at most one tile's readout positions, were issued after them)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * PER_CHUNK));
+        barrier_no_fence();
+        if (ic == nch) {  // the issue point enters the next tile
+          ic = 0;
+          ++ik;
+          wv0 = wv0_next;
+          wv0_next = w_row0(ik + 1);
+          rows(pos_next, xsrc);
+          positions(ik + 1, pos_next);
+        }
+        issue(ic, islot);  // into the slot chunk (k, c) - 1 used
+        ++ic;
+        islot = islot + 1 == NS ? 0 : islot + 1;
+      }
+      // the compute waves' epilogue barriers
+      barrier_no_fence();
+      barrier_no_fence();
+      barrier_no_fence();
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing loads land before the workgroup ends
+    return;
+  }
+
+  // ---- compute waves: fragments of chunk q from ring slot q % NS
+  int wrd[2][4], xrd[NI][4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int wr = 64 * cw + 32 * mi + ql;
+      wrd[mi][st] = wr * 64 + 8 * ((4 * g + st) ^ ((wr >> 1) & 7));
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int n = 32 * ni + ql;
+      xrd[ni][st] = n * 64 + 8 * ((4 * g + st) ^ ((n >> 1) & 7));
+    }
+  }
+  int slot = 0;
+  for (int k = 0; k < ntile; ++k) {
+    f32x16 acc[2][NI];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) acc[mi][ni][a] = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      barrier_no_fence();
+      const __bf16 *wb = ws_[slot];
+      const __bf16 *xb = xs[slot];
+      bf16x8 af[4][2], bfr[4][NI];
+      auto rd = [&](int st) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) af[st][mi] = *reinterpret_cast<const bf16x8 *>(wb + wrd[mi][st]);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) bfr[st][ni] = *reinterpret_cast<const bf16x8 *>(xb + xrd[ni][st]);
+      };
+      auto mm = [&](int st) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[st][mi], bfr[st][ni], acc[mi][ni], 0, 0, 0);
+      };
+      // k-steps in order, each a fenced group: the fragments of k-steps 0 and
+      // 1 first, then k-step st's MFMAs with the reads of k-step st + 2
+      constexpr int RD = 2 + NI, MF = 2 * NI;
+      rd(0);
+      rd(1);
+      __builtin_amdgcn_sched_barrier(0);
+      rd(2);
+      mm(0);
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      rd(3);
+      mm(1);
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mm(2);
+      mm(3);
+      __builtin_amdgcn_sched_barrier(0);
+      slot = slot + 1 == NS ? 0 : slot + 1;
+    }
+    const int vt = tile_vt(k);
+    wide_epilogue<NI>(acc, sm.red, vt * BVW, vt, tile_n0(k), V, N, labels, pmax, psum, plab);
+  }
+}
+
 // ---------------------------------------------------------------- fp32
 // One workgroup per (128 vocabulary rows, item); one thread per row.
 __global__ __launch_bounds__(BV) void score_f32_kernel(
@@ -664,7 +866,20 @@ ScoreKernel pick_score(int N, int H, mis_dtype dt, ScoreForce force, int force_n
   if (H % 64 != 0) return {ScoreKind::Global, N <= 64 ? 1 : N <= 128 ? 2 : 4};
   // Up to 64 items stream W through the narrow tiles (every LM-head row read
   // once); more items take the wide tiles, MFMA-bound.
-  const bool wide = force == ScoreForce::Wide || (force == ScoreForce::Auto && N > 64);
+  // More than 64 items: the persistent workgroups with loader waves (item
+  // blocks 3-5); the wide tiles only when forced or H < 128.
+  if ((force == ScoreForce::Persist || (force == ScoreForce::Auto && N > 64)) && H >= 128) {
+    int ni = force_ni;
+    if (ni != 3 && ni != 4 && ni != 5) {
+      ni = 3;
+      for (int c : {4, 5}) {
+        const int pc = (N + 32 * c - 1) / (32 * c) * 32 * c, pb = (N + 32 * ni - 1) / (32 * ni) * 32 * ni;
+        if (pc <= pb) ni = c;
+      }
+    }
+    return {ScoreKind::Persist, ni};
+  }
+  const bool wide = force == ScoreForce::Wide || force == ScoreForce::Persist || (force == ScoreForce::Auto && N > 64);
   if (!wide) return {ScoreKind::Narrow, N <= 32 ? 1 : N <= 64 ? 2 : 4};
   int ni = force_ni;
   if (ni != 3 && ni != 4 && ni != 5 && ni != 6 && ni != 8) {
@@ -691,6 +906,7 @@ void score_kernel_name(const ScoreKernel &k, char *buf, size_t n) {
   switch (k.kind) {
     case ScoreKind::Narrow: snprintf(buf, n, "score_lds_kernel<%d, %d>", k.ni, score_stages(k)); return;
     case ScoreKind::Wide: snprintf(buf, n, "score_wide_kernel<%d, %d>", k.ni, score_stages(k)); return;
+    case ScoreKind::Persist: snprintf(buf, n, "score_persist_kernel<%d, 3>", k.ni); return;
     case ScoreKind::Global: snprintf(buf, n, "score_bf16_kernel<%d>", k.ni); return;
     case ScoreKind::F32: snprintf(buf, n, "score_f32_kernel"); return;
   }
@@ -726,6 +942,24 @@ hipError_t launch_score(const int32_t *readout_pos, int N, const void *hidden, i
         default: return hipErrorInvalidValue;
       }
 #undef MIS_WIDE
+      nvt_used = nvw;
+      break;
+    }
+    case ScoreKind::Persist: {
+      if (H < 128) return hipErrorInvalidValue;  // the ring's first two chunks are in the first tile
+      const int nvw = (V + 255) / 256;
+      const int nit = (N + 32 * ni - 1) / (32 * ni);
+      const int tiles8 = (nvw + 7) / 8 * 8 * nit;  // tile slots over the 8 XCDs
+      const unsigned grid = unsigned(std::max(8, std::min(device_cus() / 8 * 8, tiles8)));
+#define MIS_PERSIST(NI) \
+  score_persist_kernel<NI, 3><<<grid, 512, 0, st>>>(hp, wp, H, V, N, readout_pos, labels, pmax, psum, plab, nvw, nit)
+      switch (ni) {
+        case 3: MIS_PERSIST(3); break;
+        case 4: MIS_PERSIST(4); break;
+        case 5: MIS_PERSIST(5); break;
+        default: return hipErrorInvalidValue;
+      }
+#undef MIS_PERSIST
       nvt_used = nvw;
       break;
     }

@@ -283,10 +283,15 @@ def test_kernel_choice_names_and_rejects_unknown():
     try:
         # scoring: the shapes of the five workloads, then forced variants
         assert mis.score_kernel_name(64, 1024, bf16) == "score_lds_kernel<2, 3>"
-        assert mis.score_kernel_name(300, 4096, bf16) == "score_wide_kernel<5, 3>"
-        assert mis.score_kernel_name(1024, 8192, bf16) == "score_wide_kernel<8, 2>"
+        assert mis.score_kernel_name(300, 4096, bf16) == "score_persist_kernel<5, 3>"
+        assert mis.score_kernel_name(1024, 8192, bf16) == "score_persist_kernel<4, 3>"
+        assert mis.score_kernel_name(6400, 1024, bf16) == "score_persist_kernel<5, 3>"
+        assert mis.score_kernel_name(80, 64, bf16) == "score_wide_kernel<3, 3>"  # H < 128
         assert mis.score_kernel_name(4, 256, mis.MIS_F32) == "score_f32_kernel"
         assert mis.score_kernel_name(200, 96, bf16) == "score_bf16_kernel<4>"
+        mis.set_kernel_choice(score="persist3")
+        assert mis.score_kernel_name(64, 1024, bf16) == "score_persist_kernel<3, 3>"
+        assert mis.score_kernel_name(80, 64, bf16) == "score_wide_kernel<3, 3>"  # H < 128: wide tiles
         mis.set_kernel_choice(score="wide4")
         assert mis.score_kernel_name(64, 1024, bf16) == "score_wide_kernel<4, 3>"
         mis.set_kernel_choice(score="narrow")

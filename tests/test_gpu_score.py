@@ -16,11 +16,12 @@ from gpu_common import (TOL_BF16_SCORE, TOL_F32, build, cached, dev, hidden_with
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(autouse=True, params=["auto", "narrow", "wide4", "wide6"])
+@pytest.fixture(autouse=True, params=["auto", "narrow", "wide4", "wide6", "persist3", "persist4"])
 def score_kernel(request):
     """Every case with the bf16 LM-head kernel chosen by shape (narrow tiles up
-    to 64 items, else wide tiles with 3, 5 or 8 item blocks), and forced to the
-    narrow tiles and to wide tiles of 4 and 6 item blocks."""
+    to 64 items, else the persistent wide tiles with 3, 4 or 5 item blocks),
+    and forced to the narrow tiles, to the non-persistent wide tiles of 4 and 6
+    item blocks and to the persistent ones of 3 and 4."""
     mis.set_kernel_choice(score=request.param)
     yield request.param
     mis.set_kernel_choice()
