@@ -107,6 +107,32 @@ def test_item_and_vocab_edges(dtype, n_items, vocab):
         assert np.abs(got).max() <= tol  # a one-word vocabulary has log-prob 0
 
 
+@pytest.mark.parametrize("hidden", [128, 192])
+@pytest.mark.parametrize("n_items,vocab", [(300, 120001), (97, 70000), (65, 33000), (129, 255), (70, 1)])
+def test_several_tiles_per_workgroup(hidden, n_items, vocab):
+    # The persistent kernel (more than 64 items, H >= 128) runs one workgroup
+    # per CU, so these vocabularies give most workgroups two or three tiles
+    # in a row; H = 128 and 192 make the chunk sequence cross into the next
+    # tile while the ring's first chunks are still being staged. Ragged
+    # vocabulary and item tails, a single partial vocabulary tile, a
+    # one-word vocabulary; labels at both vocabulary ends and in the middle.
+    wl = workloads.from_lengths("persist", [12], [[2] * n_items], hq=4, hkv=2, d=128, hidden=hidden,
+                                vocab=vocab, num_labels=3)
+    so = segments_oracle(wl)
+    seg = build(wl)
+    hid = hidden_with_sentinels(wl, so["readout_pos"])
+    W = workloads.lm_head(wl)
+    labels = sorted({0, vocab - 1, vocab // 2, (7 * vocab) // 9})
+    say(f"[score] persistent tiles N={n_items} V={vocab} H={hidden}")
+    got = _score(wl, seg, hid, W, labels)
+    assert np.isfinite(got).all()
+    ref = oracle.label_scores(hid, so["readout_pos"], W, labels)
+    assert np.abs(got - ref).max() <= TOL_BF16_SCORE
+    p = _score(wl, seg, hid, W, labels, apply_softmax=True)
+    refp = oracle.label_scores(hid, so["readout_pos"], W, labels, apply_softmax=True)
+    assert np.abs(p - refp).max() <= TOL_BF16_SCORE
+
+
 @pytest.mark.parametrize("hidden", [32, 96, 160])
 @pytest.mark.parametrize("n_items,vocab", [(5, 1000), (70, 129), (200, 300)])
 def test_hidden_not_a_multiple_of_64(hidden, n_items, vocab):
