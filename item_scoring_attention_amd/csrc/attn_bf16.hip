@@ -59,6 +59,7 @@
 // share it); the O rescale is skipped when no lane of the wave raised it.
 // Row sums add the bf16-rounded P (the values the PV product uses), two per
 // v_dot2_f32_bf16.
+#include <atomic>
 #include <utility>
 
 #include "gfx950_util.h"
@@ -442,15 +443,16 @@ hipError_t launch_variant(const mis_segments &seg, const __bf16 *qp, const __bf1
 
 // Compute units of the current device (queried once per device).
 int device_cus() {
-  static int cus[64] = {};
+  // per device, queried once; threads that race here store the same value
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (!n) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 AttnKernel pick_attention_bf16(const mis_segments &seg, int hq, int hkv, AttnForce force) {
