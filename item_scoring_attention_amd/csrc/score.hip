@@ -865,9 +865,9 @@ ScoreKernel pick_score(int N, int H, mis_dtype dt, ScoreForce force, int force_n
   if (dt != MIS_BF16) return {ScoreKind::F32, 1};
   if (H % 64 != 0) return {ScoreKind::Global, N <= 64 ? 1 : N <= 128 ? 2 : 4};
   // Up to 64 items stream W through the narrow tiles (every LM-head row read
-  // once); more items take the wide tiles, MFMA-bound.
-  // More than 64 items: the persistent workgroups with loader waves (item
-  // blocks 3-5); the wide tiles only when forced or H < 128.
+  // once). More items are MFMA-bound: the persistent workgroups with loader
+  // waves (item blocks 3-5, the fewest padded items, then the widest tile),
+  // or the wide tiles when forced or H < 128.
   if ((force == ScoreForce::Persist || (force == ScoreForce::Auto && N > 64)) && H >= 128) {
     int ni = force_ni;
     if (ni != 3 && ni != 4 && ni != 5) {
