@@ -277,8 +277,9 @@ def test_kernel_choice_names_and_rejects_unknown():
     mis.set_kernel_choice()
     with pytest.raises(ValueError, match="unknown attention kernel choice"):
         mis.set_kernel_choice(attention="fastest")
-    with pytest.raises(ValueError, match="unknown scoring kernel choice"):
-        mis.set_kernel_choice(score="wide7")
+    for bad in ("wide7", "persist2", "persist6", "persist8", "narrow2"):
+        with pytest.raises(ValueError, match="unknown scoring kernel choice"):
+            mis.set_kernel_choice(score=bad)
     bf16 = mis.MIS_BF16
     try:
         # scoring: the shapes of the five workloads, then forced variants
@@ -289,6 +290,12 @@ def test_kernel_choice_names_and_rejects_unknown():
         assert mis.score_kernel_name(80, 64, bf16) == "score_wide_kernel<3, 3>"  # H < 128
         assert mis.score_kernel_name(4, 256, mis.MIS_F32) == "score_f32_kernel"
         assert mis.score_kernel_name(200, 96, bf16) == "score_bf16_kernel<4>"
+        mis.set_kernel_choice(score="persist")
+        assert mis.score_kernel_name(64, 1024, bf16) == "score_persist_kernel<3, 3>"  # 96 slots, the fewest
+        assert mis.score_kernel_name(128, 1024, bf16) == "score_persist_kernel<4, 3>"  # no padding
+        assert mis.score_kernel_name(300, 4096, bf16) == "score_persist_kernel<5, 3>"
+        mis.set_kernel_choice(score="persist5")
+        assert mis.score_kernel_name(1024, 8192, bf16) == "score_persist_kernel<5, 3>"
         mis.set_kernel_choice(score="persist3")
         assert mis.score_kernel_name(64, 1024, bf16) == "score_persist_kernel<3, 3>"
         assert mis.score_kernel_name(80, 64, bf16) == "score_wide_kernel<3, 3>"  # H < 128: wide tiles
