@@ -297,9 +297,19 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
       }
     }
   }
-  // class of visit `lane` (lanes past the last visit read visit 0's tile)
-  const int kt0 = lane < n_visit ? (lane < a_end ? lane : b_start + (lane - a_end)) : (a_end > 0 ? 0 : b_start);
-  const int tc0 = tile_class[cls_base + kt0];
+  // classes of visits lane + 64 u, issued with the kernel's own loads so
+  // that their latency is paid once (lanes past the last visit read visit
+  // 0's tile); tiles with more visits scan the rest after the ring's start
+  auto visit_tile = [&](int idx) { return idx < a_end ? idx : b_start + (idx - a_end); };
+  constexpr int KCU = 8;
+  int tcs[KCU];
+#pragma unroll
+  for (int u = 0; u < KCU; ++u) {
+    const int idx = lane + 64 * u;
+    tcs[u] = 2;
+    if (u == 0 || 64 * u < n_visit)
+      tcs[u] = tile_class[cls_base + (idx < n_visit ? visit_tile(idx) : visit_tile(0))];
+  }
   // position ids of the lane's query rows (rows past the request end read the last row)
   int pos[QB];
 #pragma unroll
@@ -319,11 +329,18 @@ __global__ __launch_bounds__(64 * HP * TB, TB) void attn_pipe_kernel(
   // the request; the mask runs on every visit from a_full on.
   {
     int first = n_visit;
-    if (lane < n_visit && ((tc0 != 2) | (kt0 * BN + BN > Tr))) first = lane;
-    for (int i0 = 64; i0 < n_visit; i0 += 64) {
+#pragma unroll
+    for (int u = 0; u < KCU; ++u) {
+      const int idx = lane + 64 * u;
+      if (idx < n_visit) {
+        const int kt = visit_tile(idx);
+        if ((tcs[u] != 2) | (kt * BN + BN > Tr)) first = min(first, idx);
+      }
+    }
+    for (int i0 = 64 * KCU; i0 < n_visit; i0 += 64) {
       const int idx = i0 + lane;
       if (idx < n_visit) {
-        const int kt = idx < a_end ? idx : b_start + (idx - a_end);
+        const int kt = visit_tile(idx);
         if ((tile_class[cls_base + kt] != 2) | (kt * BN + BN > Tr)) first = min(first, idx);
       }
     }
