@@ -37,6 +37,13 @@
  *   buffer; the *_bytes queries give the sizes. mis_build_segments uploads its
  *   metadata through a small ring of page-locked host slots that the library
  *   allocates once per device and keeps until the process ends.
+ * - HIP graph capture: the attention, rotation and scoring calls enqueue
+ *   kernels only (no memory sets, copies or host waits), so they can be
+ *   captured. mis_build_segments (when its metadata does not fit in the
+ *   builder's kernel arguments) and mis_score_labels_at copy from a staging
+ *   slot that later calls reuse, so a replay could read another call's data:
+ *   run them outside capture. A segment buffer built once serves any number
+ *   of captured calls.
  * - Packed ("varlen") token-major layout: request r owns packed tokens
  *   [cu_seqlens[r], cu_seqlens[r+1]); its first prefix_lens[r] tokens are the
  *   prefix, then its items follow back to back in input order. Items are
