@@ -42,25 +42,36 @@ PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def visible_pairs(wl) -> int:
-    """(query, key) pairs the MIS mask allows, summed over requests (one head)."""
+def visible_pairs(wl, items_only: bool = False) -> int:
+    """(query, key) pairs the MIS mask allows, summed over requests (one head);
+    with ``items_only`` the item rows' pairs only (appending items to a cached
+    prefix)."""
     total = 0
     lens = wl.item_lengths()
     for r in range(wl.num_requests):
         lq = int(wl.prefix_lens[r])
         s = lens[int(wl.cu_items[r]) : int(wl.cu_items[r + 1])].astype(np.int64)
-        total += lq * (lq + 1) // 2 + int((s * lq + s * (s + 1) // 2).sum())
+        if not items_only:
+            total += lq * (lq + 1) // 2
+        total += int((s * lq + s * (s + 1) // 2).sum())
     return total
 
 
-def attention_flops(wl) -> int:
-    return 4 * wl.d * wl.hq * visible_pairs(wl)
+def attention_flops(wl, items_only: bool = False) -> int:
+    return 4 * wl.d * wl.hq * visible_pairs(wl, items_only)
 
 
-def lm_head_cost(wl):
-    flops = 2 * wl.total_items * wl.hidden * wl.vocab
-    nbytes = 2 * (wl.vocab * wl.hidden + wl.total_items * wl.hidden) + 4 * wl.total_items * wl.num_labels
+def lm_head_cost(wl, rows=None):
+    """FLOPs and algorithmic bytes of scoring ``rows`` readout rows (default:
+    one per item) against the whole vocabulary."""
+    rows = wl.total_items if rows is None else rows
+    flops = 2 * rows * wl.hidden * wl.vocab
+    nbytes = 2 * (wl.vocab * wl.hidden + rows * wl.hidden) + 4 * rows * wl.num_labels
     return flops, nbytes
+
+
+def lm_head_bound_s(flops, nbytes):
+    return max(nbytes / (PEAK_HBM_GBS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12))
 
 
 ATTN_SOURCES = ("attn_bf16.hip", "attn_bf16_pipe.hip", "attn_loop.inc")
@@ -516,6 +527,22 @@ def main(argv=None):
     # to pass + attention). The table depends on theta, D and the longest
     # request only (built once, for every layer and batch).
     n_att = max(2, min(20, int(200.0 / max(t_att_warm, 1e-3))))
+    # Items against a cached prefix: item rows only, the prefix K/V read as
+    # cached (query tiles of prefix rows only exit at once).
+    t_append = back_to_back(lambda: mis.mis_attention_append(seg, qd, kd, vd, od, stream=stream), n_att)
+    # Label scores at several marker rows per item (the last m rows of each
+    # item, m = 3 where every item is that long), host row list included.
+    m_at = int(min(3, int(wl.item_lengths().min())))
+    markers = (readout[:, None] - np.arange(m_at - 1, -1, -1)[None, :]).reshape(-1).astype(np.int64)
+    hidd[torch.from_numpy(markers).cuda()] = hidd[torch.from_numpy(np.repeat(readout, m_at).astype(np.int64)).cuda()]
+    sc_at = torch.empty((markers.size, wl.num_labels), dtype=torch.float32, device="cuda")
+    ws_at = torch.empty(mis.mis_score_workspace_bytes(markers.size, wl.vocab, wl.num_labels, wl.hidden,
+                                                      mis.MIS_BF16), dtype=torch.uint8, device="cuda")
+    t_sco_warm = float(np.mean(warm_ms["score"]))
+    n_at = max(3, min(50, int(100.0 / max(m_at * t_sco_warm, 1e-3))))
+    t_at = back_to_back(lambda: mis.mis_score_labels_at(markers, hidd, Wd, labels, scores=sc_at, ws=ws_at,
+                                                        stream=stream), n_at)
+    at_kernel = mis.score_kernel_name(int(markers.size), wl.hidden, mis.MIS_BF16)
     t_table = back_to_back(lambda: mis.mis_rope_table(seg.max_seqlen, wl.d, 1e6, table=rope_tab, stream=stream), 3)
     t_rope_k = back_to_back(lambda: mis.mis_apply_rope(seg, None, kd, 1e6, stream=stream), 10)
     t_att_plain = back_to_back(lambda: mis.mis_attention_prefill(seg, qd, kd, vd, o=od, stream=stream), n_att)
@@ -577,7 +604,7 @@ def main(argv=None):
         },
     }
     f_lm, b_lm = lm_head_cost(wl)
-    t_bound = max(b_lm / (PEAK_HBM_GBS * 1e9), f_lm / (PEAK_BF16_TFLOPS * 1e12))
+    t_bound = lm_head_bound_s(f_lm, b_lm)
     out["roofline_score"] = {
         "kernel": f"{score_kernel} + combine_kernel (LM head, split-vocab logsumexp)",
         "bound": "hbm" if b_lm / (PEAK_HBM_GBS * 1e9) >= f_lm / (PEAK_BF16_TFLOPS * 1e12) else "mfma",
@@ -600,6 +627,27 @@ def main(argv=None):
         "algorithmic_bytes_per_launch": rope_bytes,
         "k_only": {"ms": round(t_rope_k, 4), "algorithmic_bytes_per_launch": rope_k_bytes,
                    "achieved_gbs": round(rope_k_bytes / (t_rope_k * 1e-3) / 1e9, 1)},
+    }
+    f_app = attention_flops(wl, items_only=True)
+    out["append"] = {
+        "kernel": f"{attn_kernel} (items against a cached prefix, not in the step)",
+        "bound": "mfma",
+        "ms": round(t_append, 4),
+        "achieved_tflops": round(f_app / (t_append * 1e-3) / 1e12, 2),
+        "frac": round(f_app / (t_append * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_flops_per_launch": f_app,
+        "full_prefill_ms": round(t_att_plain, 4),
+    }
+    f_at, b_at = lm_head_cost(wl, rows=int(markers.size))
+    out["score_at"] = {
+        "kernel": f"{at_kernel} + combine_kernel (label scores at {m_at} marker rows per item, not in the step)",
+        "rows": int(markers.size),
+        "ms": round(t_at, 4),
+        "achieved_gbs": round(b_at / (t_at * 1e-3) / 1e9, 1),
+        "achieved_tflops": round(f_at / (t_at * 1e-3) / 1e12, 2),
+        "frac": round(lm_head_bound_s(f_at, b_at) / (t_at * 1e-3), 4),
+        "algorithmic_bytes_per_launch": b_at,
+        "algorithmic_flops_per_launch": f_at,
     }
     # attention with the rotation, both ways (back-to-back launches, same state)
     out["rope_step_ms"] = {

@@ -31,6 +31,26 @@ def test_bench_pairs_equal_the_mask(prefix, items):
     assert bench.visible_pairs(wl) == _mask_pairs(wl)
 
 
+@pytest.mark.parametrize("prefix,items", [
+    ([64], [[9, 9, 9, 9]]),
+    ([0, 37, 5], [[4, 1], [12, 3, 7], []]),
+    ([130, 1], [[1] * 20, [2, 2]]),
+])
+def test_append_pairs_are_the_item_rows_of_the_mask(prefix, items):
+    # the work of appending items to a cached prefix: the visible cells of
+    # the item rows of the explicit mask, prefix rows left out
+    wl = workloads.from_lengths("pairs", prefix, items, hq=4, hkv=2, d=64)
+    so = oracle.build_segments(wl.cu_seqlens, wl.prefix_lens, wl.cu_items, wl.item_starts)
+    ids = so["item_id"]
+    want = 0
+    for r in range(wl.num_requests):
+        a, b = int(wl.cu_seqlens[r]), int(wl.cu_seqlens[r + 1])
+        m = oracle.mis_mask(ids[a:b])
+        want += int(np.count_nonzero(m[ids[a:b] >= 0] == 0.0))
+    assert bench.visible_pairs(wl, items_only=True) == want
+    assert bench.attention_flops(wl, items_only=True) == 4 * 64 * 4 * want
+
+
 def test_tiny_workload_pairs_and_flops():
     wl = workloads.config(1)
     assert bench.visible_pairs(wl) == _mask_pairs(wl)
