@@ -393,6 +393,9 @@ def main(argv=None):
     ap.add_argument("--item-tokens", type=int, default=28, help="item length in --paper (28 chat, 24 compact)")
     ap.add_argument("--paper-n", type=lambda x: [int(t) for t in x.split(",")], default=[1, 5, 20, 50, 100, 200],
                     help="items per member in --paper")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the timings beside the step (rotary, cached-prefix append, scores at several rows "
+                         "per item), which launch the step's kernels again on other shapes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args(argv)
@@ -502,53 +505,55 @@ def main(argv=None):
             step(cold)
         torch.cuda.synchronize()
         cold_ms = split(cold)
-    print("[bench] timed; measuring the MFMA probe and the rotary kernels", file=sys.stderr, flush=True)
+    print("[bench] timed; measuring the MFMA probe" + ("" if args.no_extras else " and the calls beside the step"),
+          file=sys.stderr, flush=True)
     t_att_warm = float(np.mean(warm_ms["attention"]))
     rope_tab = torch.empty((seg.max_seqlen, wl.d), dtype=torch.float32, device="cuda")
     mfma_peak = mfma_peak_tflops(stream)
 
-    # Rotary embedding at the reused positions (in place on q and k; not in
-    # the step, timed last since it changes q and k).
-    def back_to_back(fn, n):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        fn()
-        a.record(stream)
-        for _ in range(n):
+    if not args.no_extras:
+        # Rotary embedding at the reused positions (in place on q and k; not in
+        # the step, timed last since it changes q and k).
+        def back_to_back(fn, n):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
             fn()
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) / n
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+            b.synchronize()
+            return a.elapsed_time(b) / n
 
-    t_rope = back_to_back(lambda: mis.mis_apply_rope(seg, qd, kd, 1e6, stream=stream), 10)
-    rope_bytes = 2 * wl.total_tokens * (wl.hq + wl.hkv) * wl.d * 2  # read and write q, k (bf16)
-    # The same rotation with Q turned inside the attention kernel: K alone in
-    # the pass, Q from the cos/sin table as it is loaded (outputs bit-identical
-    # to pass + attention). The table depends on theta, D and the longest
-    # request only (built once, for every layer and batch).
-    n_att = max(2, min(20, int(200.0 / max(t_att_warm, 1e-3))))
-    # Items against a cached prefix: item rows only, the prefix K/V read as
-    # cached (query tiles of prefix rows only exit at once).
-    t_append = back_to_back(lambda: mis.mis_attention_append(seg, qd, kd, vd, od, stream=stream), n_att)
-    # Label scores at several marker rows per item (the last m rows of each
-    # item, m = 3 where every item is that long), host row list included.
-    m_at = int(min(3, int(wl.item_lengths().min())))
-    markers = (readout[:, None] - np.arange(m_at - 1, -1, -1)[None, :]).reshape(-1).astype(np.int64)
-    hidd[torch.from_numpy(markers).cuda()] = hidd[torch.from_numpy(np.repeat(readout, m_at).astype(np.int64)).cuda()]
-    sc_at = torch.empty((markers.size, wl.num_labels), dtype=torch.float32, device="cuda")
-    ws_at = torch.empty(mis.mis_score_workspace_bytes(markers.size, wl.vocab, wl.num_labels, wl.hidden,
-                                                      mis.MIS_BF16), dtype=torch.uint8, device="cuda")
-    t_sco_warm = float(np.mean(warm_ms["score"]))
-    n_at = max(3, min(50, int(100.0 / max(m_at * t_sco_warm, 1e-3))))
-    t_at = back_to_back(lambda: mis.mis_score_labels_at(markers, hidd, Wd, labels, scores=sc_at, ws=ws_at,
-                                                        stream=stream), n_at)
-    at_kernel = mis.score_kernel_name(int(markers.size), wl.hidden, mis.MIS_BF16)
-    t_table = back_to_back(lambda: mis.mis_rope_table(seg.max_seqlen, wl.d, 1e6, table=rope_tab, stream=stream), 3)
-    t_rope_k = back_to_back(lambda: mis.mis_apply_rope(seg, None, kd, 1e6, stream=stream), 10)
-    t_att_plain = back_to_back(lambda: mis.mis_attention_prefill(seg, qd, kd, vd, o=od, stream=stream), n_att)
-    t_att_fused = back_to_back(lambda: mis.mis_attention_prefill_rope(seg, qd, kd, vd, rope_tab, o=od,
-                                                                      stream=stream), n_att)
-    rope_k_bytes = 2 * wl.total_tokens * wl.hkv * wl.d * 2
+        t_rope = back_to_back(lambda: mis.mis_apply_rope(seg, qd, kd, 1e6, stream=stream), 10)
+        rope_bytes = 2 * wl.total_tokens * (wl.hq + wl.hkv) * wl.d * 2  # read and write q, k (bf16)
+        # The same rotation with Q turned inside the attention kernel: K alone in
+        # the pass, Q from the cos/sin table as it is loaded (outputs bit-identical
+        # to pass + attention). The table depends on theta, D and the longest
+        # request only (built once, for every layer and batch).
+        n_att = max(2, min(20, int(200.0 / max(t_att_warm, 1e-3))))
+        # Items against a cached prefix: item rows only, the prefix K/V read as
+        # cached (query tiles of prefix rows only exit at once).
+        t_append = back_to_back(lambda: mis.mis_attention_append(seg, qd, kd, vd, od, stream=stream), n_att)
+        # Label scores at several marker rows per item (the last m rows of each
+        # item, m = 3 where every item is that long), host row list included.
+        m_at = int(min(3, int(wl.item_lengths().min())))
+        markers = (readout[:, None] - np.arange(m_at - 1, -1, -1)[None, :]).reshape(-1).astype(np.int64)
+        hidd[torch.from_numpy(markers).cuda()] = hidd[torch.from_numpy(np.repeat(readout, m_at).astype(np.int64)).cuda()]
+        sc_at = torch.empty((markers.size, wl.num_labels), dtype=torch.float32, device="cuda")
+        ws_at = torch.empty(mis.mis_score_workspace_bytes(markers.size, wl.vocab, wl.num_labels, wl.hidden,
+                                                          mis.MIS_BF16), dtype=torch.uint8, device="cuda")
+        t_sco_warm = float(np.mean(warm_ms["score"]))
+        n_at = max(3, min(50, int(100.0 / max(m_at * t_sco_warm, 1e-3))))
+        t_at = back_to_back(lambda: mis.mis_score_labels_at(markers, hidd, Wd, labels, scores=sc_at, ws=ws_at,
+                                                            stream=stream), n_at)
+        at_kernel = mis.score_kernel_name(int(markers.size), wl.hidden, mis.MIS_BF16)
+        t_table = back_to_back(lambda: mis.mis_rope_table(seg.max_seqlen, wl.d, 1e6, table=rope_tab, stream=stream), 3)
+        t_rope_k = back_to_back(lambda: mis.mis_apply_rope(seg, None, kd, 1e6, stream=stream), 10)
+        t_att_plain = back_to_back(lambda: mis.mis_attention_prefill(seg, qd, kd, vd, o=od, stream=stream), n_att)
+        t_att_fused = back_to_back(lambda: mis.mis_attention_prefill_rope(seg, qd, kd, vd, rope_tab, o=od,
+                                                                          stream=stream), n_att)
+        rope_k_bytes = 2 * wl.total_tokens * wl.hkv * wl.d * 2
 
     flops = attention_flops(wl)
     t_att = float(np.mean(warm_ms["attention"]))
@@ -617,49 +622,50 @@ def main(argv=None):
     if cold_ms:
         t_cold = float(np.mean(cold_ms["score"]))
         out["roofline_score"]["frac_cold"] = round(t_bound / (t_cold * 1e-3), 4)
-    out["roofline_rope"] = {
-        "kernel": "rope_kernel (rotary embedding of q and k at the reused positions, not in the step)",
-        "bound": "hbm",
-        "ms": round(t_rope, 4),
-        "achieved_gbs": round(rope_bytes / (t_rope * 1e-3) / 1e9, 1),
-        "peak_gbs": PEAK_HBM_GBS,
-        "frac": round(rope_bytes / (t_rope * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "algorithmic_bytes_per_launch": rope_bytes,
-        "k_only": {"ms": round(t_rope_k, 4), "algorithmic_bytes_per_launch": rope_k_bytes,
-                   "achieved_gbs": round(rope_k_bytes / (t_rope_k * 1e-3) / 1e9, 1)},
-    }
-    f_app = attention_flops(wl, items_only=True)
-    out["append"] = {
-        "kernel": f"{attn_kernel} (items against a cached prefix, not in the step)",
-        "bound": "mfma",
-        "ms": round(t_append, 4),
-        "achieved_tflops": round(f_app / (t_append * 1e-3) / 1e12, 2),
-        "frac": round(f_app / (t_append * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "algorithmic_flops_per_launch": f_app,
-        "full_prefill_ms": round(t_att_plain, 4),
-    }
-    f_at, b_at = lm_head_cost(wl, rows=int(markers.size))
-    out["score_at"] = {
-        "kernel": f"{at_kernel} + combine_kernel (label scores at {m_at} marker rows per item, not in the step)",
-        "rows": int(markers.size),
-        "ms": round(t_at, 4),
-        "achieved_gbs": round(b_at / (t_at * 1e-3) / 1e9, 1),
-        "achieved_tflops": round(f_at / (t_at * 1e-3) / 1e12, 2),
-        "frac": round(lm_head_bound_s(f_at, b_at) / (t_at * 1e-3), 4),
-        "algorithmic_bytes_per_launch": b_at,
-        "algorithmic_flops_per_launch": f_at,
-    }
-    # attention with the rotation, both ways (back-to-back launches, same state)
-    out["rope_step_ms"] = {
-        "separate": round(t_rope + t_att_plain, 4),
-        "fused": round(t_rope_k + t_att_fused, 4),
-        "rotation_pass_q_and_k": round(t_rope, 4),
-        "rotation_pass_k": round(t_rope_k, 4),
-        "attention": round(t_att_plain, 4),
-        "attention_rotating_q": round(t_att_fused, 4),
-        "table_once": round(t_table, 4),
-        "table_positions": int(seg.max_seqlen),
-    }
+    if not args.no_extras:
+        out["roofline_rope"] = {
+            "kernel": "rope_kernel (rotary embedding of q and k at the reused positions, not in the step)",
+            "bound": "hbm",
+            "ms": round(t_rope, 4),
+            "achieved_gbs": round(rope_bytes / (t_rope * 1e-3) / 1e9, 1),
+            "peak_gbs": PEAK_HBM_GBS,
+            "frac": round(rope_bytes / (t_rope * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes_per_launch": rope_bytes,
+            "k_only": {"ms": round(t_rope_k, 4), "algorithmic_bytes_per_launch": rope_k_bytes,
+                       "achieved_gbs": round(rope_k_bytes / (t_rope_k * 1e-3) / 1e9, 1)},
+        }
+        f_app = attention_flops(wl, items_only=True)
+        out["append"] = {
+            "kernel": f"{attn_kernel} (items against a cached prefix, not in the step)",
+            "bound": "mfma",
+            "ms": round(t_append, 4),
+            "achieved_tflops": round(f_app / (t_append * 1e-3) / 1e12, 2),
+            "frac": round(f_app / (t_append * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flops_per_launch": f_app,
+            "full_prefill_ms": round(t_att_plain, 4),
+        }
+        f_at, b_at = lm_head_cost(wl, rows=int(markers.size))
+        out["score_at"] = {
+            "kernel": f"{at_kernel} + combine_kernel (label scores at {m_at} marker rows per item, not in the step)",
+            "rows": int(markers.size),
+            "ms": round(t_at, 4),
+            "achieved_gbs": round(b_at / (t_at * 1e-3) / 1e9, 1),
+            "achieved_tflops": round(f_at / (t_at * 1e-3) / 1e12, 2),
+            "frac": round(lm_head_bound_s(f_at, b_at) / (t_at * 1e-3), 4),
+            "algorithmic_bytes_per_launch": b_at,
+            "algorithmic_flops_per_launch": f_at,
+        }
+        # attention with the rotation, both ways (back-to-back launches, same state)
+        out["rope_step_ms"] = {
+            "separate": round(t_rope + t_att_plain, 4),
+            "fused": round(t_rope_k + t_att_fused, 4),
+            "rotation_pass_q_and_k": round(t_rope, 4),
+            "rotation_pass_k": round(t_rope_k, 4),
+            "attention": round(t_att_plain, 4),
+            "attention_rotating_q": round(t_att_fused, 4),
+            "table_once": round(t_table, 4),
+            "table_positions": int(seg.max_seqlen),
+        }
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")  # 1 GiB
         b = torch.empty_like(a)
